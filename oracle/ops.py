@@ -1,0 +1,341 @@
+"""Plain float64 definitions of the fused non-GEMM operators.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and obviously
+correct: no blocking, no fusion, no one-pass rewrites.  Each function widens its
+fp16 / int32 inputs to float64, computes the textbook definition, and rounds
+once where the GPU path stores a value.
+
+Readings of points the pages leave open are stated in the docstrings; they are
+the same readings the library documents in its header.
+"""
+
+import numpy as np
+
+from .philox import random_fields
+
+# ----------------------------------------------------------------------------
+# Dropout decision
+# ----------------------------------------------------------------------------
+
+
+def _check_p(p):
+    p32 = float(np.float32(p))
+    if not (0.0 <= p32 <= 1.0):
+        raise ValueError("dropout probability must lie in [0, 1]")
+    return p32
+
+
+def drop_threshold(p, bits):
+    """Integer drop threshold floor(p * 2**bits) for a bits-wide random field.
+
+    p is taken as the float32 value the caller passes; p * 2**bits is exact in
+    float64, so the floor is exact.
+    """
+    return int(np.floor(_check_p(p) * float(1 << bits)))
+
+
+def dropout_scale(p, bits):
+    """Inverted-dropout scale 1 / (1 - p_eff), p_eff = threshold / 2**bits.
+
+    When every element is dropped (p_eff == 1) the scale is 0 so that the
+    output is exactly zero.
+    """
+    t = drop_threshold(p, bits)
+    if t >= (1 << bits):
+        return 0.0
+    return 1.0 / (1.0 - t / float(1 << bits))
+
+
+def dropout_keep(index, p, seed, offset, bits):
+    """Keep decision for each flat element index.
+
+    Dropout is counter based: element i of one dropout site is decided by its
+    own random field of the Philox4x32-10 stream keyed on ``seed`` with the
+    stream word ``offset`` (one offset per dropout site), so forward and
+    backward regenerate the same mask without storing it.  An element is
+    dropped iff its field is below floor(p * 2**bits).  The mask m of [LS2]
+    sec. 2.1.2 (embedding backward) is this decision times the inverted
+    scale.
+
+    index: 1-D integer array, or an int n meaning range(n).
+    Returns a bool array (True = keep).
+    """
+    if np.isscalar(index):
+        index = np.arange(int(index), dtype=np.uint64)
+    t = drop_threshold(p, bits)
+    if t == 0:
+        return np.ones(np.asarray(index).shape, dtype=bool)
+    fields = random_fields(index, bits, seed, offset)
+    return fields >= np.uint64(t)
+
+
+def _masked_scale(shape, p, seed, offset, bits):
+    """keep * scale for a row-major tensor of this shape, as float64."""
+    n = int(np.prod(shape))
+    keep = dropout_keep(n, p, seed, offset, bits)
+    return (keep.astype(np.float64) * dropout_scale(p, bits)).reshape(shape)
+
+
+# ----------------------------------------------------------------------------
+# Fused elementwise operators ([L10] technique 1, slide 12; [LS2] sec. 2.1.1)
+# ----------------------------------------------------------------------------
+
+
+def bias_dropout_residual(x, bias, residual, p, seed, offset, bits):
+    """out = residual + Dropout(x + bias), rounded once to fp16.
+
+    x, residual: fp16 [rows, cols]; bias: fp16 [cols] (broadcast over rows).
+    The element index of the dropout decision is the flat row-major index.
+    The order (bias add, then dropout, then residual add) is the one the
+    self-attention output block of [LS2] sec. 2.1.1 fuses.
+    Parity: pinned by tests (p = 0 exact sum; mask exposure with x=1, b=0, r=0;
+    keep-rate statistics).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    b64 = np.asarray(bias, dtype=np.float64)
+    r64 = np.asarray(residual, dtype=np.float64)
+    ms = _masked_scale(x64.shape, p, seed, offset, bits)
+    return (r64 + ms * (x64 + b64[None, :])).astype(np.float16)
+
+
+def bias_relu_dropout(x, bias, p, seed, offset, bits):
+    """out = Dropout(ReLU(x + bias)), rounded once to fp16 ([L10] slide 12).
+
+    x: fp16 [rows, cols]; bias: fp16 [cols].
+    Parity: pinned by tests (p = 0 equals np.maximum; zero where dropped or
+    where x + b <= 0).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    b64 = np.asarray(bias, dtype=np.float64)
+    ms = _masked_scale(x64.shape, p, seed, offset, bits)
+    return (ms * np.maximum(x64 + b64[None, :], 0.0)).astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm ([L10] technique 2, slides 21-22)
+# ----------------------------------------------------------------------------
+
+
+def layernorm_fwd(x, gamma, beta, eps):
+    """Two-pass LayerNorm over the last axis.
+
+    mean = sum(x) / H;  var = sum((x - mean)^2) / H  (biased);
+    rstd = 1 / sqrt(var + eps);  y = (x - mean) * rstd * gamma + beta.
+    The pages write sigma = sqrt(E[x^2] - E[x]^2) without eps; eps is read as
+    going inside the root, as in every training LayerNorm.
+    Returns (y fp16 [rows, H], mean fp32 [rows], rstd fp32 [rows]).
+    Parity: pinned by tests (constant row gives beta; the row (+a, -a, ...)
+    gives +-a / sqrt(a^2 + eps); torch.nn.functional.layer_norm in fp64;
+    one-pass and two-pass variance agree in fp64).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    g64 = np.asarray(gamma, dtype=np.float64)
+    b64 = np.asarray(beta, dtype=np.float64)
+    eps64 = float(np.float32(eps))
+    h = x64.shape[-1]
+    mean = x64.sum(axis=-1) / h
+    centered = x64 - mean[:, None]
+    var = (centered * centered).sum(axis=-1) / h
+    rstd = 1.0 / np.sqrt(var + eps64)
+    y = centered * rstd[:, None] * g64[None, :] + b64[None, :]
+    return y.astype(np.float16), mean.astype(np.float32), rstd.astype(np.float32)
+
+
+def layernorm_bwd(dy, x, gamma, mean, rstd):
+    """LayerNorm backward given the saved row statistics.
+
+    With xhat = (x - mean) * rstd and g = gamma * dy (per row of length H):
+      dx     = rstd * (g - sum(g)/H - xhat * sum(g * xhat)/H)
+      dgamma = sum over rows of dy * xhat
+      dbeta  = sum over rows of dy
+    This is the derivative of layernorm_fwd written out directly; [L10]
+    slide 22 regroups the same expression into two row sums that can be
+    reduced together.
+    Returns (dx fp16 [rows, H], dgamma fp16 [H], dbeta fp16 [H]).
+    Parity: pinned by tests (central finite differences through
+    layernorm_fwd; torch autograd in fp64; per-row invariants sum(dx) = 0 and
+    sum(dx * xhat) = 0).
+    """
+    dy64 = np.asarray(dy, dtype=np.float64)
+    x64 = np.asarray(x, dtype=np.float64)
+    g64 = np.asarray(gamma, dtype=np.float64)
+    mu = np.asarray(mean, dtype=np.float64)[:, None]
+    rs = np.asarray(rstd, dtype=np.float64)[:, None]
+    h = x64.shape[-1]
+    xhat = (x64 - mu) * rs
+    g = g64[None, :] * dy64
+    sum_g = g.sum(axis=-1, keepdims=True)
+    sum_gx = (g * xhat).sum(axis=-1, keepdims=True)
+    dx = rs * (g - sum_g / h - xhat * sum_gx / h)
+    dgamma = (dy64 * xhat).sum(axis=0)
+    dbeta = dy64.sum(axis=0)
+    return dx.astype(np.float16), dgamma.astype(np.float16), dbeta.astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
+# Softmax ([L10] slides 23-26)
+# ----------------------------------------------------------------------------
+
+
+def softmax_valid(batch, heads, q_len, k_len, key_lengths=None, causal=False):
+    """Boolean [batch, heads, q_len, k_len] mask of the keys a row may attend to.
+
+    Key j of query row i in sequence b is valid iff j < key_lengths[b] (when
+    given; values are clamped into [0, k_len]) and, when causal, j <= i.
+    Padding masks only keys; padded query rows still attend to the valid keys.
+    """
+    j = np.arange(k_len)[None, None, None, :]
+    valid = np.ones((batch, heads, q_len, k_len), dtype=bool)
+    if key_lengths is not None:
+        lens = np.clip(np.asarray(key_lengths, dtype=np.int64), 0, k_len)
+        valid &= j < lens[:, None, None, None]
+    if causal:
+        i = np.arange(q_len)[None, None, :, None]
+        valid &= j <= i
+    return valid
+
+
+def softmax_fwd(x, key_lengths=None, causal=False):
+    """Masked row softmax over the last axis, two passes.
+
+    x: fp16 [batch, heads, q_len, k_len].  For each row, m = max of the valid
+    entries, e_j = exp(x_j - m) on valid entries and 0 elsewhere,
+    y = e / sum(e).  A row with no valid entry is all zeros.
+    Returns y fp16 of x's shape.
+    Parity: pinned by tests (scipy.special.softmax; rows sum to one; the
+    online max/normaliser recurrence of [CS336] sec. 6.2 agrees; masked
+    entries exactly zero; constant row gives 1/|valid|).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    b, h, q, k = x64.shape
+    valid = softmax_valid(b, h, q, k, key_lengths, causal)
+    masked = np.where(valid, x64, -np.inf)
+    m = masked.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(valid, np.exp(masked - m), 0.0)
+    s = e.sum(axis=-1, keepdims=True)
+    y = np.divide(e, s, out=np.zeros_like(e), where=s > 0)
+    return y.astype(np.float16)
+
+
+def softmax_bwd(y, dy):
+    """Softmax backward from the stored output: dx = y * (dy - sum(y * dy)).
+
+    y, dy: fp16 [..., k_len]; the sum runs over the last axis.  Masked entries
+    have y = 0 and therefore dx = 0, so no mask argument is needed.
+    Returns dx fp16.
+    Parity: pinned by tests (finite differences through softmax_fwd in fp64;
+    rows of dx sum to zero; constant dy gives dx = 0).
+    """
+    y64 = np.asarray(y, dtype=np.float64)
+    dy64 = np.asarray(dy, dtype=np.float64)
+    dot = (y64 * dy64).sum(axis=-1, keepdims=True)
+    return (y64 * (dy64 - dot)).astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
+# Embedding ([LS2] sec. 2.1.2)
+# ----------------------------------------------------------------------------
+
+
+def embedding_fwd(ids, tok_emb, pos_emb, scale, p, seed, offset, bits):
+    """out[t] = Dropout(s * E[ids_t] + P[t mod L]), rounded once to fp16.
+
+    ids: int32 [batch, L]; tok_emb E: fp16 [V, H]; pos_emb P: fp16
+    [max_pos, H] with max_pos >= L; scale s (e.g. sqrt(d_model)).
+    Token t = b * L + l sits at position l.  Element (t, c) uses the flat index
+    t * H + c for its dropout decision.  A token id outside [0, V) yields a
+    row of NaN (its table row is never read).
+    Returns fp16 [batch * L, H].
+    Parity: pinned by tests (p = 0 and P = 0 give the exact gather times a
+    power-of-two scale; torch.nn.functional.embedding).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    e64 = np.asarray(tok_emb, dtype=np.float64)
+    p64 = np.asarray(pos_emb, dtype=np.float64)
+    batch, seq = ids.shape
+    vocab, hidden = e64.shape
+    flat = ids.reshape(-1)
+    ok = (flat >= 0) & (flat < vocab)
+    rows = e64[np.where(ok, flat, 0)]
+    pos = np.tile(np.arange(seq), batch)
+    s = float(np.float32(scale))
+    val = s * rows + p64[pos]
+    val = val * _masked_scale(val.shape, p, seed, offset, bits)
+    val[~ok] = np.nan
+    return val.astype(np.float16)
+
+
+def embedding_bwd(ids, dy, vocab, scale, p, seed, offset, bits, grad_in=None):
+    """grad E[w] += s * sum over tokens t with ids_t = w of m_t * dy_t.
+
+    m_t is the forward's mask (keep times the inverted scale), regenerated
+    from (seed, offset).  ids: int32 [batch, L]; dy: fp16 [batch * L, H].
+    ``grad_in`` (fp32 [V, H]) is the accumulator the caller passes; None means
+    it starts at zero.  Tokens whose id lies outside [0, V) contribute
+    nothing.  The sum is taken in float64 and rounded once to fp32.
+    Returns fp32 [V, H].
+    Parity: pinned by tests (torch autograd through an fp64 embedding lookup;
+    an id that occurs once gives exactly s * m * dy; the column sums of the
+    gradient equal s * sum of m * dy).
+    """
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    dy64 = np.asarray(dy, dtype=np.float64)
+    hidden = dy64.shape[-1]
+    dy64 = dy64.reshape(-1, hidden)
+    s = float(np.float32(scale))
+    contrib = s * dy64 * _masked_scale(dy64.shape, p, seed, offset, bits)
+    acc = np.zeros((vocab, hidden), dtype=np.float64)
+    if grad_in is not None:
+        acc += np.asarray(grad_in, dtype=np.float64)
+    ok = (ids >= 0) & (ids < vocab)
+    np.add.at(acc, ids[ok], contrib[ok])
+    return acc.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Mixed-precision Adam over the fp16 workspace ([L10] slide 29; [LS2] sec. 2.3)
+# ----------------------------------------------------------------------------
+
+
+def adam_workspace_step(param, grad, exp_avg, exp_avg_sq, lr, beta1, beta2, eps,
+                        weight_decay, step, grad_scale=1.0, decoupled_wd=True):
+    """One Adam step on fp16 parameters and gradients with fp32 moments.
+
+    The trainer of [LS2] sec. 2.3 keeps parameters and gradients only in
+    fp16 and widens them on the fly; no fp32 master copy exists.  With
+    t = step (1-based), g = grad / grad_scale (loss scaling, [CS336] 3.2):
+      (L2 form only) g += wd * p
+      m = beta1 * m + (1 - beta1) * g
+      v = beta2 * v + (1 - beta2) * g^2
+      update = (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+      (decoupled form, AdamW) update += wd * p
+      p = p - lr * update
+    The moments are rounded to fp32 when stored and the stored values feed
+    the update; the new parameter is rounded once to fp16.  Hyper-parameters
+    are taken as the float32 values the caller passes.
+    Returns (param fp16, exp_avg fp32, exp_avg_sq fp32).
+    Parity: pinned by tests (step-1 closed form; zero gradient gives
+    p * (1 - lr * wd); torch.optim.AdamW / Adam in fp64 without the storage
+    roundings).
+    """
+    f = lambda v: float(np.float32(v))  # noqa: E731
+    lr, beta1, beta2, eps, wd, gs = map(f, (lr, beta1, beta2, eps, weight_decay, grad_scale))
+    t = int(step)
+    if t < 1:
+        raise ValueError("step is 1-based")
+    p64 = np.asarray(param, dtype=np.float64)
+    g64 = np.asarray(grad, dtype=np.float64) / gs
+    m64 = np.asarray(exp_avg, dtype=np.float64)
+    v64 = np.asarray(exp_avg_sq, dtype=np.float64)
+    if not decoupled_wd:
+        g64 = g64 + wd * p64
+    m_new = (beta1 * m64 + (1.0 - beta1) * g64).astype(np.float32)
+    v_new = (beta2 * v64 + (1.0 - beta2) * g64 * g64).astype(np.float32)
+    m_hat = m_new.astype(np.float64) / (1.0 - beta1 ** t)
+    v_hat = v_new.astype(np.float64) / (1.0 - beta2 ** t)
+    update = m_hat / (np.sqrt(v_hat) + eps)
+    if decoupled_wd:
+        update = update + wd * p64
+    p_new = (p64 - lr * update).astype(np.float16)
+    return p_new, m_new, v_new

@@ -1,0 +1,411 @@
+"""Pins for the oracle's operator definitions (CPU only).
+
+Each check is independent of the oracle's own code: closed forms, library
+routines (torch / scipy on the CPU in float64), brute force, finite
+differences, and invariants the mathematics fixes.
+"""
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle.ops import dropout_keep, dropout_scale
+
+BITS = 16
+SEED = 0x0123456789ABCDEF
+
+
+def f16(a):
+    return np.asarray(a, dtype=np.float16)
+
+
+# ----------------------------------------------------------------------------
+# bias + dropout + residual, bias + ReLU + dropout
+# ----------------------------------------------------------------------------
+
+def test_bdr_p0_is_rounded_sum():
+    g = np.random.default_rng(1)
+    x, r = f16(g.normal(size=(37, 24))), f16(g.normal(size=(37, 24)))
+    b = f16(g.normal(0, 0.02, size=24))
+    out = oracle.bias_dropout_residual(x, b, r, 0.0, SEED, 0, BITS)
+    ref = (x.astype(np.float64) + b.astype(np.float64) + r.astype(np.float64)).astype(np.float16)
+    np.testing.assert_array_equal(out, ref)
+
+
+def test_bdr_exposes_mask():
+    """x = 1, b = 0, r = 0: out is the scale where kept and 0 where dropped, in
+    flat row-major order (checks that bias broadcasts over rows, the residual is
+    added outside the dropout, and the element index is row * cols + col)."""
+    rows, cols = 16, 40
+    x = np.ones((rows, cols), np.float16)
+    out = oracle.bias_dropout_residual(x, np.zeros(cols, np.float16), np.zeros_like(x), 0.3, SEED, 5, BITS)
+    keep = dropout_keep(rows * cols, 0.3, SEED, 5, BITS).reshape(rows, cols)
+    scale = 1.0 / (1.0 - np.floor(np.float64(np.float32(0.3)) * 65536) / 65536)
+    np.testing.assert_array_equal(out, np.where(keep, scale, 0.0).astype(np.float16))
+    # residual survives where the branch is dropped
+    r = np.full((rows, cols), 2.0, np.float16)
+    out2 = oracle.bias_dropout_residual(x, np.zeros(cols, np.float16), r, 0.3, SEED, 5, BITS)
+    assert (out2[~keep] == 2.0).all()
+    # bias is added before the dropout scale
+    b = np.full(cols, 1.0, np.float16)
+    out3 = oracle.bias_dropout_residual(x, b, np.zeros_like(x), 0.3, SEED, 5, BITS)
+    np.testing.assert_array_equal(out3, np.where(keep, 2 * scale, 0.0).astype(np.float16))
+
+
+def test_brd_p0_and_zeros():
+    g = np.random.default_rng(2)
+    x = f16(g.normal(size=(33, 48)))
+    b = f16(g.normal(0, 0.5, size=48))
+    out = oracle.bias_relu_dropout(x, b, 0.0, SEED, 1, BITS)
+    ref = np.maximum(x.astype(np.float64) + b.astype(np.float64), 0).astype(np.float16)
+    np.testing.assert_array_equal(out, ref)
+    out = oracle.bias_relu_dropout(x, b, 0.25, SEED, 1, BITS)
+    keep = dropout_keep(x.size, 0.25, SEED, 1, BITS).reshape(x.shape)
+    pre = x.astype(np.float64) + b.astype(np.float64)
+    assert (out[~keep] == 0).all() and (out[pre <= 0] == 0).all()
+    sel = keep & (pre > 0)
+    np.testing.assert_allclose(out[sel].astype(np.float64), pre[sel] / (1 - 16384 / 65536), rtol=1e-3)
+
+
+def test_dropout_all_dropped():
+    x = np.ones((4, 8), np.float16)
+    out = oracle.bias_relu_dropout(x, np.zeros(8, np.float16), 1.0, SEED, 0, BITS)
+    assert (out == 0).all()
+    out = oracle.bias_dropout_residual(x, np.zeros(8, np.float16), x, 1.0, SEED, 0, BITS)
+    assert (out == 1).all()
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm
+# ----------------------------------------------------------------------------
+
+def test_ln_constant_row_gives_beta():
+    h = 64
+    x = np.full((3, h), 1.5, np.float16)
+    g = np.random.default_rng(3)
+    gamma, beta = f16(g.uniform(0.5, 1.5, h)), f16(g.normal(0, 0.1, h))
+    y, mean, rstd = oracle.layernorm_fwd(x, gamma, beta, 1e-5)
+    np.testing.assert_array_equal(y, np.broadcast_to(beta, y.shape))
+    assert (mean == np.float32(1.5)).all()
+    np.testing.assert_allclose(rstd, 1 / np.sqrt(np.float64(np.float32(1e-5))), rtol=1e-7)
+
+
+def test_ln_plus_minus_row_closed_form():
+    """Row (a, -a, a, -a, ...): mean 0, var a^2, y = +-a/sqrt(a^2 + eps)."""
+    a, h, eps = 0.75, 32, 1e-5
+    x = f16(np.tile([a, -a], h // 2)[None, :])
+    gamma = np.ones(h, np.float16)
+    beta = np.zeros(h, np.float16)
+    y, mean, rstd = oracle.layernorm_fwd(x, gamma, beta, eps)
+    expect = np.tile([a, -a], h // 2) / np.sqrt(a * a + np.float64(np.float32(eps)))
+    np.testing.assert_array_equal(y[0], expect.astype(np.float16))
+    assert mean[0] == 0.0
+
+
+def test_ln_matches_torch_and_one_pass():
+    g = np.random.default_rng(4)
+    x = f16(g.normal(0.3, 1.7, size=(50, 96)))
+    gamma, beta = f16(g.uniform(0.5, 1.5, 96)), f16(g.normal(0, 0.1, 96))
+    eps = 1e-5
+    y, mean, rstd = oracle.layernorm_fwd(x, gamma, beta, eps)
+    xt = torch.tensor(x.astype(np.float64))
+    ref = torch.nn.functional.layer_norm(xt, (96,), torch.tensor(gamma.astype(np.float64)),
+                                         torch.tensor(beta.astype(np.float64)), float(np.float32(eps)))
+    np.testing.assert_array_equal(y, ref.numpy().astype(np.float16))
+    # one-pass statistics (E[x^2] - E[x]^2) agree with the two-pass ones in fp64
+    x64 = x.astype(np.float64)
+    mu1 = x64.mean(1)
+    var1 = (x64 * x64).mean(1) - mu1 * mu1
+    np.testing.assert_allclose(1 / np.sqrt(var1 + np.float64(np.float32(eps))), rstd, rtol=1e-6)
+    np.testing.assert_allclose(mu1, mean, rtol=1e-6, atol=1e-7)
+
+
+def _ln_fwd64(x, gamma, beta, eps):
+    mu = x.mean(-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+@pytest.mark.parametrize("rows,h", [(3, 8), (2, 16)])
+def test_ln_bwd_finite_differences(rows, h):
+    """Central differences of sum(dy * LN(x)) in fp64 (h = 1e-6)."""
+    g = np.random.default_rng(5 + h)
+    x = f16(g.normal(size=(rows, h)))
+    dy = f16(g.normal(size=(rows, h)))
+    gamma, beta = f16(g.uniform(0.5, 1.5, h)), f16(g.normal(0, 0.1, h))
+    eps = float(np.float32(1e-5))
+    x64, dy64, g64, b64 = (a.astype(np.float64) for a in (x, dy, gamma, beta))
+    mu = x64.mean(-1)
+    rstd = 1 / np.sqrt(((x64 - mu[:, None]) ** 2).mean(-1) + eps)
+    dx, dgamma, dbeta = oracle.layernorm_bwd(dy, x, gamma, mu, rstd)
+
+    def loss(xx, gg, bb):
+        return (dy64 * _ln_fwd64(xx, gg, bb, eps)).sum()
+    step = 1e-6
+    num_dx = np.zeros_like(x64)
+    for i in range(rows):
+        for j in range(h):
+            e = np.zeros_like(x64)
+            e[i, j] = step
+            num_dx[i, j] = (loss(x64 + e, g64, b64) - loss(x64 - e, g64, b64)) / (2 * step)
+    num_dg = np.array([(loss(x64, g64 + step * np.eye(h)[j], b64) - loss(x64, g64 - step * np.eye(h)[j], b64))
+                       / (2 * step) for j in range(h)])
+    num_db = np.array([(loss(x64, g64, b64 + step * np.eye(h)[j]) - loss(x64, g64, b64 - step * np.eye(h)[j]))
+                       / (2 * step) for j in range(h)])
+    np.testing.assert_allclose(dx.astype(np.float64), num_dx, rtol=2e-3, atol=2e-3)
+    np.testing.assert_allclose(dgamma.astype(np.float64), num_dg, rtol=2e-3, atol=2e-3)
+    np.testing.assert_allclose(dbeta.astype(np.float64), num_db, rtol=2e-3, atol=2e-3)
+
+
+def test_ln_bwd_torch_autograd_and_invariants():
+    g = np.random.default_rng(6)
+    rows, h = 40, 64
+    x = f16(g.normal(size=(rows, h)))
+    dy = f16(g.normal(size=(rows, h)))
+    gamma, beta = f16(g.uniform(0.5, 1.5, h)), f16(g.normal(0, 0.1, h))
+    eps = float(np.float32(1e-5))
+    xt = torch.tensor(x.astype(np.float64), requires_grad=True)
+    gt = torch.tensor(gamma.astype(np.float64), requires_grad=True)
+    bt = torch.tensor(beta.astype(np.float64), requires_grad=True)
+    y = torch.nn.functional.layer_norm(xt, (h,), gt, bt, eps)
+    y.backward(torch.tensor(dy.astype(np.float64)))
+    x64 = x.astype(np.float64)
+    mu = x64.mean(-1)
+    rstd = 1 / np.sqrt(((x64 - mu[:, None]) ** 2).mean(-1) + eps)
+    dx, dgamma, dbeta = oracle.layernorm_bwd(dy, x, gamma, mu, rstd)
+    np.testing.assert_array_equal(dx, xt.grad.numpy().astype(np.float16))
+    np.testing.assert_array_equal(dgamma, gt.grad.numpy().astype(np.float16))
+    np.testing.assert_array_equal(dbeta, bt.grad.numpy().astype(np.float16))
+    # invariants of the exact gradient; sum(dx * xhat) = 0 needs eps = 0
+    rstd0 = 1 / np.sqrt(((x64 - mu[:, None]) ** 2).mean(-1))
+    dx0 = oracle.layernorm_bwd(dy, x, gamma, mu, rstd0)[0]
+    xhat = (x64 - mu[:, None]) * rstd0[:, None]
+    gd = gamma.astype(np.float64) * dy.astype(np.float64)
+    dx64 = rstd0[:, None] * (gd - gd.mean(-1, keepdims=True) - xhat * (gd * xhat).mean(-1, keepdims=True))
+    np.testing.assert_array_equal(dx0, dx64.astype(np.float16))
+    np.testing.assert_allclose(dx64.sum(-1), 0, atol=1e-10)
+    np.testing.assert_allclose((dx64 * xhat).sum(-1), 0, atol=1e-10)
+    np.testing.assert_array_equal(dbeta, dy.astype(np.float64).sum(0).astype(np.float16))
+
+
+# ----------------------------------------------------------------------------
+# Softmax
+# ----------------------------------------------------------------------------
+
+def test_softmax_matches_scipy_dense():
+    g = np.random.default_rng(7)
+    x = f16(g.normal(0, 3, size=(2, 3, 5, 40)))
+    y = oracle.softmax_fwd(x)
+    ref = scipy.special.softmax(x.astype(np.float64), axis=-1)
+    np.testing.assert_array_equal(y, ref.astype(np.float16))
+    # rows sum to 1 within fp16 rounding of each entry
+    s = y.astype(np.float64).sum(-1)
+    assert np.all(np.abs(s - 1) <= 40 * 2.0 ** -11 + 1e-12)
+
+
+def test_softmax_masked_scipy_and_zeros():
+    g = np.random.default_rng(8)
+    b, h, q, k = 3, 2, 6, 24
+    x = f16(g.normal(0, 3, size=(b, h, q, k)))
+    lens = np.array([24, 5, 0], np.int32)
+    y = oracle.softmax_fwd(x, lens, causal=True)
+    for bi in range(b):
+        for hi in range(h):
+            for qi in range(q):
+                n = min(int(lens[bi]), qi + 1)
+                row = y[bi, hi, qi]
+                assert (row[n:] == 0).all()
+                if n:
+                    ref = scipy.special.softmax(x[bi, hi, qi, :n].astype(np.float64))
+                    np.testing.assert_array_equal(row[:n], ref.astype(np.float16))
+    assert (y[2] == 0).all()                                  # no valid key at all
+    # constant row: 1/|valid| ; shift invariance
+    c = np.zeros((1, 1, 1, 24), np.float16)
+    np.testing.assert_array_equal(oracle.softmax_fwd(c, np.array([7], np.int32))[0, 0, 0, :7],
+                                  np.float16(1 / 7))
+
+
+def test_softmax_online_recurrence_agrees():
+    """Block-wise running max m and normaliser l (online softmax) reach the
+    same normaliser as the two-pass form; the oracle's rows equal exp(x-m)/l."""
+    g = np.random.default_rng(9)
+    x = g.normal(0, 3, size=(20, 256)).astype(np.float16).astype(np.float64)
+    m = np.full(20, -np.inf)
+    l = np.zeros(20)
+    for blk in np.split(x, 8, axis=1):
+        m_new = np.maximum(m, blk.max(1))
+        l = l * np.exp(m - m_new) + np.exp(blk - m_new[:, None]).sum(1)
+        m = m_new
+    online = np.exp(x - m[:, None]) / l[:, None]
+    y = oracle.softmax_fwd(f16(x)[None, None])[0, 0]
+    np.testing.assert_array_equal(y, online.astype(np.float16))
+    # argmax of the output equals argmax of the input (lowest index on ties)
+    assert (np.argmax(x, 1) == np.argmax(y.astype(np.float64), 1)).mean() > 0.9
+
+
+def test_softmax_shift_invariance():
+    g = np.random.default_rng(10)
+    x = g.integers(-20, 20, size=(1, 1, 4, 32)).astype(np.float16)   # exact under +8
+    y1 = oracle.softmax_fwd(x)
+    y2 = oracle.softmax_fwd(f16(x.astype(np.float64) + 8))
+    np.testing.assert_array_equal(y1, y2)
+
+
+def test_softmax_bwd_finite_differences_and_invariants():
+    g = np.random.default_rng(11)
+    k = 12
+    x = g.normal(0, 1, size=(1, 1, 2, k))
+    dy = g.normal(size=(2, k))
+    y64 = scipy.special.softmax(x[0, 0], axis=-1)
+    dx = oracle.softmax_bwd(y64, dy).astype(np.float64)
+    num = np.zeros((2, k))
+    h = 1e-6
+    for i in range(2):
+        for j in range(k):
+            e = np.zeros(k)
+            e[j] = h
+            num[i, j] = ((scipy.special.softmax(x[0, 0, i] + e) * dy[i]).sum()
+                         - (scipy.special.softmax(x[0, 0, i] - e) * dy[i]).sum()) / (2 * h)
+    np.testing.assert_allclose(dx, num, rtol=2e-3, atol=1e-3)
+    # torch autograd
+    xt = torch.tensor(x[0, 0], requires_grad=True)
+    torch.softmax(xt, -1).backward(torch.tensor(dy))
+    np.testing.assert_array_equal(oracle.softmax_bwd(y64, dy), xt.grad.numpy().astype(np.float16))
+    # constant dy -> 0 ; rows of the exact gradient sum to 0
+    np.testing.assert_array_equal(oracle.softmax_bwd(y64, np.ones((2, k))), np.zeros((2, k), np.float16))
+    exact = y64 * (dy - (y64 * dy).sum(-1, keepdims=True))
+    np.testing.assert_allclose(exact.sum(-1), 0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Embedding
+# ----------------------------------------------------------------------------
+
+def test_embedding_fwd_exact_gather():
+    """p = 0 and P = 0: out = s * E[ids], exact for a power-of-two scale."""
+    g = np.random.default_rng(12)
+    v, h, b, l = 50, 16, 3, 7
+    E = f16(g.normal(0, 0.25, size=(v, h)))
+    ids = g.integers(0, v, size=(b, l)).astype(np.int32)
+    out = oracle.embedding_fwd(ids, E, np.zeros((l, h), np.float16), 32.0, 0.0, SEED, 3, BITS)
+    np.testing.assert_array_equal(out, (E[ids.reshape(-1)].astype(np.float64) * 32).astype(np.float16))
+    # against torch's embedding with positions and dropout applied by hand
+    P = f16(g.normal(size=(l + 3, h)))
+    out = oracle.embedding_fwd(ids, E, P, 32.0, 0.2, SEED, 3, BITS)
+    emb = torch.nn.functional.embedding(torch.tensor(ids.reshape(-1).astype(np.int64)),
+                                        torch.tensor(E.astype(np.float64))).numpy()
+    pos = np.tile(np.arange(l), b)
+    keep = dropout_keep(b * l * h, 0.2, SEED, 3, BITS).reshape(b * l, h)
+    ref = (32 * emb + P[pos].astype(np.float64)) * keep * dropout_scale(0.2, BITS)
+    np.testing.assert_array_equal(out, ref.astype(np.float16))
+
+
+def test_embedding_fwd_invalid_id_is_nan_row():
+    E = np.ones((4, 8), np.float16)
+    ids = np.array([[0, 4, -1, 3]], np.int32)
+    out = oracle.embedding_fwd(ids, E, np.zeros((4, 8), np.float16), 1.0, 0.0, SEED, 3, BITS)
+    assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
+    assert (out[0] == 1).all() and (out[3] == 1).all()
+
+
+def test_embedding_bwd_torch_autograd_and_conservation():
+    g = np.random.default_rng(13)
+    v, h, b, l = 40, 24, 4, 9
+    ids = g.integers(0, 8, size=(b, l)).astype(np.int32)      # many repeats
+    dy = f16(g.normal(size=(b * l, h)))
+    s, p = 32.0, 0.1
+    grad = oracle.embedding_bwd(ids, dy, v, s, p, SEED, 3, BITS)
+    keep = dropout_keep(b * l * h, p, SEED, 3, BITS).reshape(b * l, h)
+    m = keep * dropout_scale(p, BITS)
+    Et = torch.zeros((v, h), dtype=torch.float64, requires_grad=True)
+    out = s * torch.nn.functional.embedding(torch.tensor(ids.reshape(-1).astype(np.int64)), Et) * torch.tensor(m)
+    out.backward(torch.tensor(dy.astype(np.float64)))
+    np.testing.assert_array_equal(grad, Et.grad.numpy().astype(np.float32))
+    # mass conservation and untouched rows
+    contrib = s * m * dy.astype(np.float64)
+    err = np.abs(grad.astype(np.float64).sum(0) - contrib.sum(0))
+    assert np.all(err <= 1e-6 * np.abs(contrib).sum(0))        # fp32 rounding of each row only
+    assert (grad[8:] == 0).all()
+
+
+def test_embedding_bwd_single_occurrence_and_accumulate():
+    dy = f16(np.arange(16).reshape(2, 8) / 8)
+    ids = np.array([[3, 1]], np.int32)
+    grad = oracle.embedding_bwd(ids, dy, 5, 32.0, 0.0, SEED, 3, BITS)
+    np.testing.assert_array_equal(grad[3], (32 * dy[0].astype(np.float64)).astype(np.float32))
+    np.testing.assert_array_equal(grad[1], (32 * dy[1].astype(np.float64)).astype(np.float32))
+    acc = oracle.embedding_bwd(ids, dy, 5, 32.0, 0.0, SEED, 3, BITS, grad_in=grad)
+    np.testing.assert_array_equal(acc, 2 * grad)
+    bad = oracle.embedding_bwd(np.array([[7, -2]], np.int32), dy, 5, 32.0, 0.0, SEED, 3, BITS)
+    assert (bad == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# Adam
+# ----------------------------------------------------------------------------
+
+def test_adam_step1_closed_form():
+    """At t = 1, m_hat = g and v_hat = g^2, so the step is lr*(g/(|g|+eps) + wd*p)."""
+    g = np.random.default_rng(14)
+    p = f16(g.normal(0, 0.02, 1000))
+    gr = f16(g.normal(0, 1e-3, 1000))
+    lr, wd, eps = 1e-4, 0.01, 1e-8
+    p1, m1, v1 = oracle.adam_workspace_step(p, gr, np.zeros(1000, np.float32), np.zeros(1000, np.float32),
+                                            lr, 0.9, 0.98, eps, wd, 1)
+    p64, g64 = p.astype(np.float64), gr.astype(np.float64)
+    lr64, wd64, eps64 = (float(np.float32(v)) for v in (lr, wd, eps))
+    expect = p64 - lr64 * (g64 / (np.abs(g64) + eps64) + wd64 * p64)
+    np.testing.assert_array_equal(p1, expect.astype(np.float16))
+    np.testing.assert_allclose(m1, (1 - np.float64(np.float32(0.9))) * g64, rtol=1e-6)
+
+
+def test_adam_zero_grad_is_pure_decay():
+    p = f16(np.linspace(-2, 2, 64))
+    z = np.zeros(64, np.float16)
+    p1, m1, v1 = oracle.adam_workspace_step(p, z, np.zeros(64, np.float32), np.zeros(64, np.float32),
+                                            0.5, 0.9, 0.98, 1e-8, 0.1, 1)
+    lr, wd = float(np.float32(0.5)), float(np.float32(0.1))
+    np.testing.assert_array_equal(p1, (p.astype(np.float64) * (1 - lr * wd)).astype(np.float16))
+    assert (m1 == 0).all() and (v1 == 0).all()
+
+
+@pytest.mark.parametrize("decoupled", [True, False])
+def test_adam_matches_torch_optim(decoupled):
+    """Ten steps against torch.optim.AdamW / Adam in fp64.  The oracle's fp16
+    parameter storage is undone by feeding torch the same fp16-rounded
+    parameter each step and comparing one step at a time."""
+    g = np.random.default_rng(15)
+    n = 512
+    p = f16(g.normal(0, 0.02, n))
+    gr = f16(g.normal(0, 1e-3, n))
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    hyper = dict(lr=1e-3, betas=(0.9, 0.98), eps=1e-8, weight_decay=0.01)
+    f32 = lambda a: float(np.float32(a))  # noqa: E731
+    t_hyper = dict(lr=f32(1e-3), betas=(f32(0.9), f32(0.98)), eps=f32(1e-8), weight_decay=f32(0.01))
+    pt = torch.tensor(p.astype(np.float64), requires_grad=True)
+    opt = (torch.optim.AdamW if decoupled else torch.optim.Adam)([pt], **t_hyper)
+    for step in range(1, 11):
+        with torch.no_grad():
+            pt.copy_(torch.tensor(p.astype(np.float64)))
+        pt.grad = torch.tensor(gr.astype(np.float64))
+        opt.step()
+        p, m, v = oracle.adam_workspace_step(p, gr, m, v, hyper["lr"], 0.9, 0.98, 1e-8, 0.01, step,
+                                             decoupled_wd=decoupled)
+        st = opt.state[pt]
+        np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-6, atol=1e-12)
+        np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-6, atol=1e-16)
+        d = np.abs(p.astype(np.float64) - pt.detach().numpy())
+        assert np.all(d <= np.spacing(np.abs(pt.detach().numpy()).astype(np.float16)).astype(np.float64))
+
+
+def test_adam_grad_scale():
+    p = f16(np.linspace(-1, 1, 32))
+    gr = f16(np.linspace(-1, 1, 32) * 1e-3)
+    z = np.zeros(32, np.float32)
+    a = oracle.adam_workspace_step(p, gr, z, z, 1e-3, 0.9, 0.98, 1e-8, 0.0, 3, grad_scale=1.0)
+    b = oracle.adam_workspace_step(p, f16(gr.astype(np.float64) * 512), z, z, 1e-3, 0.9, 0.98, 1e-8, 0.0, 3,
+                                   grad_scale=512.0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-6)
