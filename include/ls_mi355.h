@@ -1,0 +1,211 @@
+/*
+ * ls_mi355 -- fused memory-bound non-GEMM Transformer operators for MI355X
+ * (gfx950, CDNA4), hand-written HIP behind a plain C ABI.
+ *
+ * Sources (cited by page title and section):
+ *   [L10]   CMU 11-868 L10 digest, "Accelerating Transformer on GPU: where
+ *           LightSeq saves its time" (quidproquo.cc): technique 1, kernel
+ *           fusion (slide 12); technique 2, formula rewriting for LayerNorm
+ *           and softmax (slides 21-26); technique 3, the fp16 workspace
+ *           trainer (slide 29).
+ *   [LS2]   "LightSeq2: Accelerated Training for Transformer-based Models
+ *           on GPUs", reading notes (arcsin2.cloud): sec. 2.1.1 (operator
+ *           classes, fused bias/dropout/residual), sec. 2.1.2 (embedding
+ *           forward and backward equations), sec. 2.3 (mixed-precision
+ *           trainer, symbolic tensor linking).
+ *   [CS336] Stanford CS336 lecture 5 notes, "GPU" (auss.cc): sec. 3.2
+ *           (loss scaling).
+ *   [SC11]  Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3"
+ *           (Philox4x32-10).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense and row-major.  "fp16" means IEEE binary16 storage,
+ *    passed as void*; all arithmetic is fp32 in registers, results are
+ *    rounded to fp16 with round-to-nearest-even.  fp16 subnormals are kept.
+ *  - Every tensor pointer is a DEVICE pointer into memory the caller owns.
+ *    The library never allocates, frees or synchronises; it keeps no device
+ *    state.  `stream` is a hipStream_t passed as void* (NULL = null stream);
+ *    every call only enqueues work on it.
+ *  - Each call validates its arguments on the host first and returns a
+ *    non-zero ls_status without launching anything if they are invalid; the
+ *    reason is available from ls_last_error() (thread-local).  A failed
+ *    launch returns LS_ERR_HIP.  Faults inside a kernel surface at the
+ *    caller's next synchronisation, as usual for HIP.
+ *  - A tensor with zero elements is a valid no-op (its pointers may then be
+ *    NULL).  Negative sizes are LS_ERR_SHAPE.
+ *  - Unaligned pointers (not 16-byte aligned) or a last dimension that is not
+ *    a multiple of 8 select a slower element-wise path; they are not errors.
+ *  - Aliasing: the pairs named in each comment may be the same buffer; any
+ *    other overlap is undefined.
+ *  - Calls are re-entrant and thread-safe.
+ *
+ * Dropout
+ * -------
+ *  Dropout is inverted (kept values are scaled by 1/(1-p_eff) at training
+ *  time) and counter based: element i of a dropout site is decided by a
+ *  16-bit field of Philox4x32-10 [SC11] with key (lo32(seed), hi32(seed))
+ *  and counter (lo32(i/8), hi32(i/8), lo32(offset), hi32(offset)); field
+ *  i%8 is taken from output word (i%8)/2, low half first.  The element is
+ *  dropped iff field < floor(p * 65536), so p_eff = floor(p*65536)/65536
+ *  (|p - p_eff| < 2^-16).  `offset` separates dropout sites that share a
+ *  seed.  The same (seed, offset) regenerates the same mask in a backward
+ *  pass, so no mask is stored.  i is the flat row-major index of the
+ *  operator's output element.  p must lie in [0, 1]; p = 1 drops everything.
+ */
+#ifndef LS_MI355_H
+#define LS_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LS_OK = 0,
+    LS_ERR_NULL = 1,          /* a required pointer is NULL                  */
+    LS_ERR_SHAPE = 2,         /* a size is negative, zero where not allowed,
+                                 or too large for the index arithmetic       */
+    LS_ERR_PARAM = 3,         /* a scalar argument is out of its domain      */
+    LS_ERR_WORKSPACE = 4,     /* caller-provided workspace is too small      */
+    LS_ERR_UNSUPPORTED = 5,   /* shape outside what the kernels implement    */
+    LS_ERR_HIP = 6,           /* the HIP runtime reported an error           */
+    LS_ERR_UNIMPLEMENTED = 7
+} ls_status;
+
+/* Fused bias + dropout + residual ([L10] technique 1; [LS2] sec. 2.1.1, the
+ * fused tail of the self-attention block):
+ *     out[r,c] = residual[r,c] + keep(r*cols+c) * (x[r,c] + bias[c]) / (1-p_eff)
+ * x, residual, out: fp16 [rows, cols]; bias: fp16 [cols].
+ * out may alias x or residual.  p in [0, 1]. */
+int ls_bias_dropout_residual(void* out, const void* x, const void* bias, const void* residual,
+                             int64_t rows, int64_t cols, float p, uint64_t seed, uint64_t offset,
+                             void* stream);
+
+/* Fused bias + ReLU + dropout ([L10] technique 1, slide 12):
+ *     out[r,c] = keep(r*cols+c) * max(x[r,c] + bias[c], 0) / (1-p_eff)
+ * x, out: fp16 [rows, cols]; bias: fp16 [cols].  out may alias x. */
+int ls_bias_relu_dropout(void* out, const void* x, const void* bias, int64_t rows, int64_t cols,
+                         float p, uint64_t seed, uint64_t offset, void* stream);
+
+/* LayerNorm forward with one fused reduction pass ([L10] technique 2,
+ * slide 21): per row, S1 = sum x and S2 = sum x^2 are reduced together;
+ * mean = S1/H, var = max(S2/H - mean^2, 0), rstd = 1/sqrt(var + eps),
+ * y = (x - mean) * rstd * gamma + beta.
+ * x, y: fp16 [rows, hidden]; gamma, beta: fp16 [hidden];
+ * mean, rstd: fp32 [rows] (saved for the backward).  y may alias x.
+ * eps > 0.  hidden must be in [1, 4096]. */
+int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const void* gamma,
+                     const void* beta, int64_t rows, int64_t hidden, float eps, void* stream);
+
+/* Bytes of device scratch that ls_layernorm_bwd needs for this shape
+ * (per-block fp32 column partials of dgamma and dbeta).  Depends only on
+ * (rows, hidden).  Returns 0 for invalid or empty shapes. */
+size_t ls_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
+
+/* LayerNorm backward ([L10] technique 2, slide 22).  With
+ * xhat = (x - mean) * rstd and g = gamma * dy, the two row sums
+ * A = sum g and B = sum g * xhat are reduced together, then
+ *     dx = rstd * (g - A/H - xhat * B/H).
+ * dgamma = sum_rows dy * xhat and dbeta = sum_rows dy are reduced over rows
+ * in a fixed order (bit-reproducible run to run).
+ * dy, x, dx: fp16 [rows, hidden]; gamma: fp16 [hidden]; dgamma, dbeta: fp16
+ * [hidden]; mean, rstd: fp32 [rows] from ls_layernorm_fwd.  dx may alias dy.
+ * workspace: device scratch of at least ls_layernorm_bwd_workspace_bytes()
+ * bytes, 16-byte aligned; its contents on entry are ignored.
+ * Two kernel launches (row pass, then column finalisation). */
+int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
+                     const void* gamma, const float* mean, const float* rstd, int64_t rows,
+                     int64_t hidden, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Masked row softmax forward ([L10] slides 23-26) over attention scores
+ * x, y: fp16 [batch, heads, q_len, k_len].  For row (b, h, i) the valid keys
+ * are j < key_lengths[b] (clamped to [0, k_len]; all keys if key_lengths is
+ * NULL) and, if causal != 0, j <= i.  y = exp(x - max) / sum(exp(x - max))
+ * over valid keys, exactly 0 elsewhere; a row with no valid key is all 0.
+ * key_lengths: device int32 [batch] or NULL.  y may alias x.
+ * Rows longer than one wavefront's registers use a multi-wave path; k_len
+ * must be at most 65536 (at most 1024 when it is not a multiple of 8). */
+int ls_softmax_fwd(void* y, const void* x, int64_t batch, int64_t heads, int64_t q_len,
+                   int64_t k_len, const int32_t* key_lengths, int causal, void* stream);
+
+/* Softmax backward from the stored output: dx = y * (dy - sum_j y_j dy_j)
+ * per row.  y, dy, dx: fp16 [rows, k_len].  dx may alias dy.  Same k_len
+ * limits as the forward. */
+int ls_softmax_bwd(void* dx, const void* y, const void* dy, int64_t rows, int64_t k_len,
+                   void* stream);
+
+/* Embedding forward ([LS2] sec. 2.1.2): for token t = b*seq_len + l,
+ *     out[t, c] = keep(t*hidden + c) * (scale * tok_emb[ids[t], c] + pos_emb[l, c]) / (1-p_eff)
+ * ids: device int32 [batch, seq_len]; tok_emb: fp16 [vocab, hidden];
+ * pos_emb: fp16 [max_pos, hidden] with max_pos >= seq_len;
+ * out: fp16 [batch*seq_len, hidden].  A token id outside [0, vocab) reads
+ * nothing and yields a row of NaN. */
+int ls_embedding_fwd(void* out, const int32_t* ids, const void* tok_emb, const void* pos_emb,
+                     int64_t batch, int64_t seq_len, int64_t hidden, int64_t vocab,
+                     int64_t max_pos, float scale, float p, uint64_t seed, uint64_t offset,
+                     void* stream);
+
+/* Embedding backward ([LS2] sec. 2.1.2): for every token t with id w,
+ *     grad_tok_emb[w, c] += scale * keep(t*hidden + c) / (1-p_eff) * dy[t, c]
+ * accumulated with fp32 atomic adds (repeated ids collide on one row), after
+ * duplicate ids inside each block of tokens have been summed in registers.
+ * grad_tok_emb: fp32 [vocab, hidden]; if zero_first != 0 it is zeroed first
+ * (by a fill kernel on the same stream), otherwise the call accumulates.
+ * dy: fp16 [batch*seq_len, hidden].  (seed, offset, p) must be those of the
+ * forward.  Ids outside [0, vocab) contribute nothing.  The summation order
+ * of the atomics is not fixed, so results agree to fp32 rounding, not bit
+ * for bit, between runs. */
+int ls_embedding_bwd(float* grad_tok_emb, const int32_t* ids, const void* dy, int64_t batch,
+                     int64_t seq_len, int64_t hidden, int64_t vocab, float scale, float p,
+                     uint64_t seed, uint64_t offset, int zero_first, void* stream);
+
+/* One Adam step over one contiguous fp16 parameter/gradient workspace in a
+ * single kernel launch ([L10] technique 3, slide 29; [LS2] sec. 2.3): fp16
+ * parameters and gradients are widened to fp32 in registers, updated, and
+ * the parameter is rounded back to fp16; no fp32 master copy exists.  With
+ * t = step (>= 1) and g = grad / grad_scale ([CS336] sec. 3.2):
+ *     (decoupled_wd == 0: g += weight_decay * p)
+ *     m = beta1 m + (1-beta1) g ;  v = beta2 v + (1-beta2) g^2
+ *     u = (m / (1-beta1^t)) / (sqrt(v / (1-beta2^t)) + eps)
+ *     (decoupled_wd != 0: u += weight_decay * p)     -- AdamW
+ *     p = p - lr * u
+ * param, grad: fp16 [n]; exp_avg, exp_avg_sq: fp32 [n].
+ * Constraints: lr >= 0, 0 <= beta1, beta2 < 1, eps > 0, weight_decay >= 0,
+ * grad_scale > 0, step >= 1. */
+int ls_adam_workspace_step(void* param, const void* grad, float* exp_avg, float* exp_avg_sq,
+                           int64_t n, float lr, float beta1, float beta2, float eps,
+                           float weight_decay, int64_t step, float grad_scale, int decoupled_wd,
+                           void* stream);
+
+/* --- test and introspection ------------------------------------------- */
+
+/* keep[i] = 1 if element i is kept, 0 if dropped, for i in [0, n), using
+ * exactly the decision every dropout kernel above makes.  keep: device
+ * uint8 [n]. */
+int ls_dropout_mask(uint8_t* keep, int64_t n, float p, uint64_t seed, uint64_t offset,
+                    void* stream);
+
+/* Width in bits of the random field behind one dropout decision (16). */
+int ls_dropout_decision_bits(void);
+
+/* Static text for a status code. */
+const char* ls_status_string(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* ls_last_error(void);
+
+/* Thread-local name of the kernel specialisation the last successful call on
+ * this thread launched (e.g. "layernorm_fwd/lpr32_vpl3"). */
+const char* ls_last_dispatch(void);
+
+/* Library version string. */
+const char* ls_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LS_MI355_H */

@@ -1,0 +1,405 @@
+// Embedding forward and backward ([LS2] sec. 2.1.2).
+//
+// Forward:  out[t] = Dropout(s * E[id_t] + P[t mod L]) -- a row gather fused
+// with the scale, the position add and the dropout, one pass over the output.
+//
+// Backward: dE[w] += s * sum_{t: id_t = w} m_t * dy_t with the dropout mask
+// m regenerated from (seed, offset).  Repeated ids collide on one row of dE,
+// so the sum is accumulated with fp32 atomic adds.  Each wave first takes a
+// chunk of 16 consecutive tokens, sorts their ids inside the wave (bitonic
+// network over lane shuffles), and walks the tokens in id order, adding the
+// rows of equal ids in registers; only one atomic per (distinct id, column)
+// of the chunk reaches memory.  With Zipf-distributed ids the frequent ids
+// repeat inside a chunk, which cuts the atomic count and the contention on
+// the hottest rows.
+#include "ls_common.hpp"
+
+namespace ls {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <int LPR, int NCH, bool DROP>
+__global__ __launch_bounds__(kBlock) void emb_fwd_vec_kernel(half_t* out, const int32_t* ids,
+                                                             const half_t* E, const half_t* P,
+                                                             uint32_t tokens, uint32_t h,
+                                                             uint32_t vocab, FastDiv seq,
+                                                             float scale, Dropout d) {
+    constexpr int RPW = kWave / LPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int l = lane % LPR;
+    const int sub = lane / LPR;
+    const uint32_t nv = h / 8;
+    for (uint32_t t0 = blockIdx.x * (kWaves * RPW); t0 < tokens; t0 += gridDim.x * (kWaves * RPW)) {
+        const uint32_t t = t0 + wave * RPW + sub;
+        if (t >= tokens) continue;
+        const int32_t id = ids[t];
+        const bool valid = id >= 0 && static_cast<uint32_t>(id) < vocab;
+        const uint32_t pos = seq.mod(t);
+        const half8* erow = reinterpret_cast<const half8*>(E + static_cast<size_t>(valid ? id : 0) * h);
+        const half8* prow = reinterpret_cast<const half8*>(P + static_cast<size_t>(pos) * h);
+        half8* orow = reinterpret_cast<half8*>(out + static_cast<size_t>(t) * h);
+        half8 ev[NCH], pv[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t cv = l + j * LPR;
+            if (cv < nv) {
+                if (valid) ev[j] = erow[cv];
+                pv[j] = prow[cv];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t cv = l + j * LPR;
+            if (cv < nv) {
+                float o[8];
+                if (valid) {
+                    float e[8], p[8], f[8];
+                    unpack8(ev[j], e);
+                    unpack8(pv[j], p);
+                    if (DROP) {
+                        dropout_factors8(d, static_cast<uint64_t>(t) * nv + cv, f);
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) f[k] = 1.0f;
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) o[k] = fmaf(scale, e[k], p[k]) * f[k];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) o[k] = __builtin_nanf("");
+                }
+                orow[cv] = pack8(o);
+            }
+        }
+    }
+}
+
+// Element-wise fallback (unaligned tables or hidden % 8 != 0).
+template <bool DROP>
+__global__ __launch_bounds__(kBlock) void emb_fwd_scalar_kernel(half_t* out, const int32_t* ids,
+                                                                const half_t* E, const half_t* P,
+                                                                uint64_t n, uint32_t h,
+                                                                uint32_t vocab, uint32_t seq,
+                                                                float scale, Dropout d) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+        const uint64_t t = i / h;
+        const uint32_t c = static_cast<uint32_t>(i - t * h);
+        const int32_t id = ids[t];
+        float o;
+        if (id >= 0 && static_cast<uint32_t>(id) < vocab) {
+            const float e = static_cast<float>(E[static_cast<size_t>(id) * h + c]);
+            const float p = static_cast<float>(P[static_cast<size_t>(t % seq) * h + c]);
+            o = fmaf(scale, e, p) * (DROP ? dropout_factor1(d, i) : 1.0f);
+        } else {
+            o = __builtin_nanf("");
+        }
+        out[i] = static_cast<half_t>(o);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+constexpr int kChunk = 16;          // tokens per wave
+constexpr uint64_t kNoToken = ~0ull;
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Ascending bitonic sort of one 64-bit key per lane across the wave.
+__device__ __forceinline__ uint64_t wave_sort(uint64_t key, int lane) {
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t other = shfl_xor_u64(key, j);
+            const bool ascending = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            const uint64_t lo = key < other ? key : other;
+            const uint64_t hi = key < other ? other : key;
+            key = (lower == ascending) ? lo : hi;
+        }
+    }
+    return key;
+}
+
+// Wave = (chunk of kChunk tokens, all columns); lane l owns column vectors
+// l, l+64, ...  Keys are (id << 8 | local token); invalid ids sort last.
+template <int NV, bool DROP>
+__global__ __launch_bounds__(kBlock) void emb_bwd_chunk_kernel(float* dE, const int32_t* ids,
+                                                               const half_t* dy, uint32_t tokens,
+                                                               uint32_t h, uint32_t vocab,
+                                                               float scale, Dropout d) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t chunk = blockIdx.x * kWaves + threadIdx.x / kWave;
+    const uint32_t t0 = chunk * kChunk;
+    if (t0 >= tokens) return;
+    const uint32_t nv = h / 8;
+
+    uint64_t key = kNoToken;
+    if (lane < kChunk && t0 + lane < tokens) {
+        const int32_t id = ids[t0 + lane];
+        if (id >= 0 && static_cast<uint32_t>(id) < vocab)
+            key = (static_cast<uint64_t>(id) << 8) | static_cast<uint32_t>(lane);
+    }
+    key = wave_sort(key, lane);
+    const uint64_t next = __shfl_down(static_cast<unsigned long long>(key), 1);
+    const bool seg_end = lane == kWave - 1 || (next >> 8) != (key >> 8);
+    const uint64_t ends = __ballot(seg_end);
+    const int count = __popcll(__ballot(key != kNoToken));
+
+    // Fetch the chunk's gradient rows in sorted order, all loads in flight at once.
+    half8 buf[kChunk][NV];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        if (j < count) {
+            const uint64_t kj = readlane_u64(key, j);
+            const uint32_t t = t0 + static_cast<uint32_t>(kj & 0xFF);
+            const half8* row = reinterpret_cast<const half8*>(dy + static_cast<size_t>(t) * h);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t cv = lane + v * kWave;
+                if (cv < nv) buf[j][v] = row[cv];
+            }
+        }
+    }
+    float acc[NV][8];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[v][k] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        if (j < count) {
+            const uint64_t kj = readlane_u64(key, j);
+            const uint32_t t = t0 + static_cast<uint32_t>(kj & 0xFF);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t cv = lane + v * kWave;
+                if (cv < nv) {
+                    float g[8], f[8];
+                    unpack8(buf[j][v], g);
+                    if (DROP) {
+                        dropout_factors8(d, static_cast<uint64_t>(t) * nv + cv, f);
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) f[k] = 1.0f;
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) acc[v][k] = fmaf(g[k] * f[k], scale, acc[v][k]);
+                }
+            }
+            if ((ends >> j) & 1ull) {
+                float* row = dE + static_cast<size_t>(kj >> 8) * h;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const uint32_t cv = lane + v * kWave;
+                    if (cv < nv) {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            unsafeAtomicAdd(row + cv * 8 + k, acc[v][k]);
+                            acc[v][k] = 0.0f;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Element-wise fallback: one atomic per element.
+template <bool DROP>
+__global__ __launch_bounds__(kBlock) void emb_bwd_scalar_kernel(float* dE, const int32_t* ids,
+                                                                const half_t* dy, uint64_t n,
+                                                                uint32_t h, uint32_t vocab,
+                                                                float scale, Dropout d) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+        const uint64_t t = i / h;
+        const uint32_t c = static_cast<uint32_t>(i - t * h);
+        const int32_t id = ids[t];
+        if (id < 0 || static_cast<uint32_t>(id) >= vocab) continue;
+        const float f = DROP ? dropout_factor1(d, i) : 1.0f;
+        unsafeAtomicAdd(dE + static_cast<size_t>(id) * h + c, static_cast<float>(dy[i]) * f * scale);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* p, uint64_t n) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t n4 = (reinterpret_cast<uintptr_t>(p) & 15u) == 0 ? n / 4 : 0;
+    float4v* p4 = reinterpret_cast<float4v*>(p);
+    const uint64_t tid = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    for (uint64_t i = tid; i < n4; i += stride) p4[i] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (uint64_t i = n4 * 4 + tid; i < n; i += stride) p[i] = 0.0f;
+}
+
+unsigned grid_cap(uint64_t blocks, unsigned cap) {
+    return static_cast<unsigned>(blocks == 0 ? 1 : (blocks < cap ? blocks : cap));
+}
+
+struct EmbShape {
+    int lpr, nch;
+    const char* name;
+};
+
+bool emb_shape(int64_t h, EmbShape* s) {
+    const int64_t nv = h / 8;
+    if (nv <= 8) *s = {8, 1, "lpr8_nch1"};
+    else if (nv <= 16) *s = {16, 1, "lpr16_nch1"};
+    else if (nv <= 32) *s = {16, 2, "lpr16_nch2"};
+    else if (nv <= 64) *s = {32, 2, "lpr32_nch2"};
+    else if (nv <= 96) *s = {32, 3, "lpr32_nch3"};
+    else if (nv <= 128) *s = {64, 2, "lpr64_nch2"};
+    else if (nv <= 256) *s = {64, 4, "lpr64_nch4"};
+    else if (nv <= 512) *s = {64, 8, "lpr64_nch8"};
+    else return false;
+    return true;
+}
+
+#define LS_EMB_FWD(LPR, NCH)                                                                    \
+    do {                                                                                        \
+        if (drop)                                                                               \
+            emb_fwd_vec_kernel<LPR, NCH, true><<<grid, kBlock, 0, st>>>(o16, ids, E16, P16, t32, h32, v32, sdiv, scale, d); \
+        else                                                                                    \
+            emb_fwd_vec_kernel<LPR, NCH, false><<<grid, kBlock, 0, st>>>(o16, ids, E16, P16, t32, h32, v32, sdiv, scale, d); \
+    } while (0)
+
+}  // namespace
+}  // namespace ls
+
+extern "C" {
+
+int ls_embedding_fwd(void* out, const int32_t* ids, const void* tok_emb, const void* pos_emb,
+                     int64_t batch, int64_t seq_len, int64_t hidden, int64_t vocab,
+                     int64_t max_pos, float scale, float p, uint64_t seed, uint64_t offset,
+                     void* stream) {
+    using namespace ls;
+    const char* name = "ls_embedding_fwd";
+    if (batch < 0 || seq_len < 0 || hidden < 0 || vocab < 0 || max_pos < 0)
+        return fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    Dropout d;
+    if (!make_dropout(p, seed, offset, &d))
+        return fail(LS_ERR_PARAM, "%s: dropout probability %g outside [0, 1]", name, (double)p);
+    if (!host_finite(scale)) return fail(LS_ERR_PARAM, "%s: scale must be finite", name);
+    if (batch == 0 || seq_len == 0 || hidden == 0) {
+        set_dispatch("empty");
+        return LS_OK;
+    }
+    if (max_pos < seq_len) return fail(LS_ERR_SHAPE, "%s: max_pos %lld < seq_len %lld", name,
+                                       (long long)max_pos, (long long)seq_len);
+    if (vocab >= (1ll << 31) || hidden >= (1ll << 31) || batch > INT32_MAX / seq_len)
+        return fail(LS_ERR_SHAPE, "%s: sizes must be < 2^31", name);
+    if (!out || !ids || !pos_emb || (vocab > 0 && !tok_emb)) return fail(LS_ERR_NULL, "%s: null pointer", name);
+    const int64_t tokens = batch * seq_len;
+    const bool drop = d.thr != 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto* o16 = static_cast<half_t*>(out);
+    auto* E16 = static_cast<const half_t*>(tok_emb);
+    auto* P16 = static_cast<const half_t*>(pos_emb);
+    const uint32_t t32 = static_cast<uint32_t>(tokens), h32 = static_cast<uint32_t>(hidden),
+                   v32 = static_cast<uint32_t>(vocab);
+    EmbShape s;
+    const bool vec = hidden % 8 == 0 && aligned16(out) && aligned16(tok_emb) && aligned16(pos_emb) &&
+                     emb_shape(hidden, &s);
+    clear_hip_error();
+    if (vec) {
+        const FastDiv sdiv(static_cast<uint32_t>(seq_len));
+        const int64_t per_block = kWaves * (kWave / s.lpr);
+        const unsigned grid = grid_cap((tokens + per_block - 1) / per_block, 1u << 20);
+        if (s.lpr == 8) LS_EMB_FWD(8, 1);
+        else if (s.lpr == 16 && s.nch == 1) LS_EMB_FWD(16, 1);
+        else if (s.lpr == 16) LS_EMB_FWD(16, 2);
+        else if (s.lpr == 32 && s.nch == 2) LS_EMB_FWD(32, 2);
+        else if (s.lpr == 32) LS_EMB_FWD(32, 3);
+        else if (s.nch == 2) LS_EMB_FWD(64, 2);
+        else if (s.nch == 4) LS_EMB_FWD(64, 4);
+        else LS_EMB_FWD(64, 8);
+        char buf[96];
+        snprintf(buf, sizeof(buf), "embedding_fwd/%s%s", s.name, drop ? "" : "_p0");
+        set_dispatch(buf);
+    } else {
+        const uint64_t n = static_cast<uint64_t>(tokens) * static_cast<uint64_t>(hidden);
+        const unsigned grid = grid_cap((n + kBlock - 1) / kBlock, 65536);
+        if (drop)
+            emb_fwd_scalar_kernel<true><<<grid, kBlock, 0, st>>>(o16, ids, E16, P16, n, h32, v32,
+                                                                 static_cast<uint32_t>(seq_len), scale, d);
+        else
+            emb_fwd_scalar_kernel<false><<<grid, kBlock, 0, st>>>(o16, ids, E16, P16, n, h32, v32,
+                                                                  static_cast<uint32_t>(seq_len), scale, d);
+        set_dispatch("embedding_fwd/scalar");
+    }
+    return launch_status(name);
+}
+
+int ls_embedding_bwd(float* grad_tok_emb, const int32_t* ids, const void* dy, int64_t batch,
+                     int64_t seq_len, int64_t hidden, int64_t vocab, float scale, float p,
+                     uint64_t seed, uint64_t offset, int zero_first, void* stream) {
+    using namespace ls;
+    const char* name = "ls_embedding_bwd";
+    if (batch < 0 || seq_len < 0 || hidden < 0 || vocab < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    Dropout d;
+    if (!make_dropout(p, seed, offset, &d))
+        return fail(LS_ERR_PARAM, "%s: dropout probability %g outside [0, 1]", name, (double)p);
+    if (!host_finite(scale)) return fail(LS_ERR_PARAM, "%s: scale must be finite", name);
+    if (vocab >= (1ll << 31) || hidden >= (1ll << 31) || (seq_len > 0 && batch > INT32_MAX / seq_len))
+        return fail(LS_ERR_SHAPE, "%s: sizes must be < 2^31", name);
+    const int64_t tokens = batch * seq_len;
+    const uint64_t table = static_cast<uint64_t>(vocab) * static_cast<uint64_t>(hidden);
+    if (table == 0 || (tokens == 0 && !zero_first)) {
+        set_dispatch("empty");
+        return LS_OK;
+    }
+    if (!grad_tok_emb || (tokens > 0 && (!ids || !dy))) return fail(LS_ERR_NULL, "%s: null pointer", name);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    clear_hip_error();
+    if (zero_first) {
+        fill_zero_kernel<<<grid_cap((table / 4 + kBlock - 1) / kBlock, 8192), kBlock, 0, st>>>(grad_tok_emb, table);
+        const int rc = launch_status(name);
+        if (rc != LS_OK || tokens == 0) {
+            set_dispatch("embedding_bwd/zero_only");
+            return rc;
+        }
+    }
+    const bool drop = d.thr != 0;
+    const uint32_t t32 = static_cast<uint32_t>(tokens), h32 = static_cast<uint32_t>(hidden),
+                   v32 = static_cast<uint32_t>(vocab);
+    auto* dy16 = static_cast<const half_t*>(dy);
+    const bool vec = hidden % 8 == 0 && hidden <= 1024 && aligned16(dy);
+    if (vec) {
+        const uint32_t chunks = (t32 + kChunk - 1) / kChunk;
+        const unsigned grid = (chunks + kWaves - 1) / kWaves;
+        const int nv = static_cast<int>((hidden / 8 + kWave - 1) / kWave);
+        if (nv == 1) {
+            if (drop) emb_bwd_chunk_kernel<1, true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
+            else emb_bwd_chunk_kernel<1, false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
+        } else {
+            if (drop) emb_bwd_chunk_kernel<2, true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
+            else emb_bwd_chunk_kernel<2, false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
+        }
+        set_dispatch(nv == 1 ? "embedding_bwd/chunk16_nv1" : "embedding_bwd/chunk16_nv2");
+    } else {
+        const uint64_t n = static_cast<uint64_t>(tokens) * static_cast<uint64_t>(hidden);
+        const unsigned grid = grid_cap((n + kBlock - 1) / kBlock, 65536);
+        if (drop) emb_bwd_scalar_kernel<true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, n, h32, v32, scale, d);
+        else emb_bwd_scalar_kernel<false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, n, h32, v32, scale, d);
+        set_dispatch("embedding_bwd/scalar");
+    }
+    return launch_status(name);
+}
+
+}  // extern "C"

@@ -1,0 +1,432 @@
+// LayerNorm forward and backward ([L10] technique 2, slides 21-22).
+//
+// Forward: one fused reduction per row.  Each lane accumulates S1 = sum x
+// and S2 = sum x^2 over its elements; the two sums travel through the same
+// DPP/swizzle reduction, so the row needs a single cross-lane pass instead
+// of "mean first, then variance":  var = S2/H - (S1/H)^2 (clamped at 0).
+//
+// Backward: the two row sums A = sum gamma*dy and B = sum gamma*dy*xhat are
+// likewise reduced together, then dx = rstd * (gamma*dy - A/H - xhat*B/H).
+// dgamma / dbeta are column sums over all rows: every block keeps per-lane
+// fp32 column accumulators in registers over the rows it owns, folds them
+// across its waves in a fixed order through LDS, and writes one partial row
+// per block; a second kernel sums the partial rows in a fixed order, so the
+// result is bit-reproducible.
+//
+// Rows are mapped to aligned groups of LPR lanes (LPR = 8..64), each lane
+// holding NCH chunks of CW consecutive elements (CW = 8: one 16-byte access
+// per chunk; CW = 1: the element-wise path for unaligned rows).  Chunk j of
+// lane l starts at column (l + j*LPR)*CW, so at every j the LPR lanes of a
+// row read one contiguous span.
+#include "ls_common.hpp"
+
+namespace ls {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+
+template <int CW>
+struct Chunk;
+
+template <>
+struct Chunk<8> {
+    static __device__ __forceinline__ void load(const half_t* p, size_t i, float f[8]) {
+        unpack8(*reinterpret_cast<const half8*>(p + i), f);
+    }
+    static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[8]) {
+        *reinterpret_cast<half8*>(p + i) = pack8(f);
+    }
+};
+
+template <>
+struct Chunk<1> {
+    static __device__ __forceinline__ void load(const half_t* p, size_t i, float f[1]) {
+        f[0] = static_cast<float>(p[i]);
+    }
+    static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[1]) {
+        p[i] = static_cast<half_t>(f[0]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <int LPR, int NCH, int CW>
+__global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, float* rstd,
+                                                        const half_t* x, const half_t* gamma,
+                                                        const half_t* beta, uint32_t rows,
+                                                        uint32_t h, float eps) {
+    constexpr int RPW = kWave / LPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int l = lane % LPR;
+    const int sub = lane / LPR;
+
+    float g[NCH][CW], b[NCH][CW];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const uint32_t c = (l + j * LPR) * CW;
+        if (c < h) {
+            Chunk<CW>::load(gamma, c, g[j]);
+            Chunk<CW>::load(beta, c, b[j]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < CW; ++k) g[j][k] = b[j][k] = 0.0f;
+        }
+    }
+    const float hf = static_cast<float>(h);
+    for (uint32_t r0 = blockIdx.x * (kWaves * RPW); r0 < rows; r0 += gridDim.x * (kWaves * RPW)) {
+        const uint32_t row = r0 + wave * RPW + sub;
+        const bool ok = row < rows;
+        const size_t base = static_cast<size_t>(row) * h;
+        float v[NCH][CW];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            if (ok && c < h) {
+                Chunk<CW>::load(x, base + c, v[j]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < CW; ++k) v[j][k] = 0.0f;
+            }
+        }
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int k = 0; k < CW; ++k) {
+                s1 += v[j][k];
+                s2 = fmaf(v[j][k], v[j][k], s2);
+            }
+        s1 = group_sum<LPR>(s1);          // the one fused reduction: (S1, S2) together
+        s2 = group_sum<LPR>(s2);
+        const float mu = s1 / hf;
+        const float var = fmaxf(s2 / hf - mu * mu, 0.0f);
+        const float rs = rsqrtf(var + eps);
+        if (ok && l == 0) {
+            mean[row] = mu;
+            rstd[row] = rs;
+        }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            if (ok && c < h) {
+                float o[CW];
+#pragma unroll
+                for (int k = 0; k < CW; ++k) o[k] = fmaf((v[j][k] - mu) * rs, g[j][k], b[j][k]);
+                Chunk<CW>::store(y, base + c, o);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, row pass
+// ---------------------------------------------------------------------------
+template <int LPR, int NCH, int CW>
+__global__ __launch_bounds__(kBlock) void ln_bwd_kernel(half_t* dx, float* partial,
+                                                        const half_t* dy, const half_t* x,
+                                                        const half_t* gamma, const float* mean,
+                                                        const float* rstd, uint32_t rows,
+                                                        uint32_t h) {
+    constexpr int RPW = kWave / LPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int l = lane % LPR;
+    const int sub = lane / LPR;
+    extern __shared__ float lds[];     // [2][h]: fixed-order fold of the waves' column sums
+
+    float g[NCH][CW], acc_g[NCH][CW], acc_b[NCH][CW];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const uint32_t c = (l + j * LPR) * CW;
+        if (c < h) {
+            Chunk<CW>::load(gamma, c, g[j]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < CW; ++k) g[j][k] = 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < CW; ++k) acc_g[j][k] = acc_b[j][k] = 0.0f;
+    }
+    const float inv_h = 1.0f / static_cast<float>(h);
+    for (uint32_t r0 = blockIdx.x * (kWaves * RPW); r0 < rows; r0 += gridDim.x * (kWaves * RPW)) {
+        const uint32_t row = r0 + wave * RPW + sub;
+        const bool ok = row < rows;
+        const size_t base = static_cast<size_t>(row) * h;
+        float vdy[NCH][CW], vx[NCH][CW];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            if (ok && c < h) {
+                Chunk<CW>::load(dy, base + c, vdy[j]);
+                Chunk<CW>::load(x, base + c, vx[j]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < CW; ++k) vdy[j][k] = vx[j][k] = 0.0f;
+            }
+        }
+        const float mu = ok ? mean[row] : 0.0f;
+        const float rs = ok ? rstd[row] : 0.0f;
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int k = 0; k < CW; ++k) {
+                const float xh = (vx[j][k] - mu) * rs;
+                const float gd = g[j][k] * vdy[j][k];
+                vx[j][k] = xh;                         // keep xhat
+                sa += gd;
+                sb = fmaf(gd, xh, sb);
+                acc_g[j][k] = fmaf(vdy[j][k], xh, acc_g[j][k]);
+                acc_b[j][k] += vdy[j][k];
+            }
+        sa = group_sum<LPR>(sa);          // the two row sums, reduced together
+        sb = group_sum<LPR>(sb);
+        const float ca = sa * inv_h, cb = sb * inv_h;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            if (ok && c < h) {
+                float o[CW];
+#pragma unroll
+                for (int k = 0; k < CW; ++k)
+                    o[k] = rs * (g[j][k] * vdy[j][k] - fmaf(vx[j][k], cb, ca));
+                Chunk<CW>::store(dx, base + c, o);
+            }
+        }
+    }
+
+    // Fold the RPW row groups of this wave (lanes l, l+LPR, ... own the same columns).
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int k = 0; k < CW; ++k)
+#pragma unroll
+            for (int o = LPR; o < kWave; o <<= 1) {
+                acc_g[j][k] += __shfl_xor(acc_g[j][k], o);
+                acc_b[j][k] += __shfl_xor(acc_b[j][k], o);
+            }
+    // Fold the waves in order 0, 1, 2, 3 through LDS.
+    for (int w = 0; w < kWaves; ++w) {
+        if (wave == w && sub == 0) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                if (c < h) {
+#pragma unroll
+                    for (int k = 0; k < CW; ++k) {
+                        lds[c + k] = (w == 0 ? 0.0f : lds[c + k]) + acc_g[j][k];
+                        lds[h + c + k] = (w == 0 ? 0.0f : lds[h + c + k]) + acc_b[j][k];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* out = partial + static_cast<size_t>(blockIdx.x) * 2 * h;
+    for (uint32_t c = threadIdx.x; c < 2 * h; c += kBlock) out[c] = lds[c];
+}
+
+// Column finalisation: dgamma[c] = sum_b partial[b][0][c], dbeta likewise.
+// 16 slices of blocks are summed by 16 thread rows, then the slices in order.
+constexpr int kFinSlices = 16;
+__global__ __launch_bounds__(kFinSlices * 64) void ln_bwd_finalize_kernel(half_t* dgamma,
+                                                                          half_t* dbeta,
+                                                                          const float* partial,
+                                                                          uint32_t nblocks,
+                                                                          uint32_t h) {
+    __shared__ float sg[kFinSlices][64], sb[kFinSlices][64];
+    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
+    const uint32_t c = blockIdx.x * 64 + cl;
+    float ag = 0.0f, ab = 0.0f;
+    if (c < h) {
+        for (uint32_t bidx = k; bidx < nblocks; bidx += kFinSlices) {
+            const float* p = partial + static_cast<size_t>(bidx) * 2 * h;
+            ag += p[c];
+            ab += p[h + c];
+        }
+    }
+    sg[k][cl] = ag;
+    sb[k][cl] = ab;
+    __syncthreads();
+    if (k == 0 && c < h) {
+        float tg = 0.0f, tb = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kFinSlices; ++s) {
+            tg += sg[s][cl];
+            tb += sb[s][cl];
+        }
+        dgamma[c] = static_cast<half_t>(tg);
+        dbeta[c] = static_cast<half_t>(tb);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch-shape table: (LPR, NCH, CW) from the row length.
+// ---------------------------------------------------------------------------
+struct LnShape {
+    int lpr, nch, cw;
+    const char* name;
+};
+
+bool ln_shape(int64_t h, bool vec, LnShape* s) {
+    if (vec) {
+        const int64_t nv = h / 8;
+        if (nv <= 8) *s = {8, 1, 8, "lpr8_nch1_v8"};
+        else if (nv <= 16) *s = {16, 1, 8, "lpr16_nch1_v8"};
+        else if (nv <= 32) *s = {16, 2, 8, "lpr16_nch2_v8"};
+        else if (nv <= 64) *s = {32, 2, 8, "lpr32_nch2_v8"};
+        else if (nv <= 96) *s = {32, 3, 8, "lpr32_nch3_v8"};
+        else if (nv <= 128) *s = {32, 4, 8, "lpr32_nch4_v8"};
+        else if (nv <= 256) *s = {64, 4, 8, "lpr64_nch4_v8"};
+        else if (nv <= 512) *s = {64, 8, 8, "lpr64_nch8_v8"};
+        else return false;
+    } else {
+        if (h <= 64) *s = {64, 1, 1, "lpr64_nch1_s"};
+        else if (h <= 128) *s = {64, 2, 1, "lpr64_nch2_s"};
+        else if (h <= 256) *s = {64, 4, 1, "lpr64_nch4_s"};
+        else if (h <= 512) *s = {64, 8, 1, "lpr64_nch8_s"};
+        else if (h <= 1024) *s = {64, 16, 1, "lpr64_nch16_s"};
+        else if (h <= 2048) *s = {64, 32, 1, "lpr64_nch32_s"};
+        else if (h <= 4096) *s = {64, 64, 1, "lpr64_nch64_s"};
+        else return false;
+    }
+    return true;
+}
+
+constexpr int64_t kMaxHidden = 4096;
+constexpr unsigned kMaxBwdBlocks = 256;
+
+unsigned fwd_grid(int64_t rows, const LnShape& s) {
+    const int64_t per_block = kWaves * (kWave / s.lpr);
+    const int64_t g = (rows + per_block - 1) / per_block;
+    return static_cast<unsigned>(g < (1 << 20) ? g : (1 << 20));
+}
+
+unsigned bwd_grid(int64_t rows, int64_t h) {
+    LnShape s;
+    if (!ln_shape(h, h % 8 == 0, &s)) ln_shape(h, false, &s);
+    const int64_t per_block = kWaves * (kWave / s.lpr);
+    const int64_t g = (rows + per_block - 1) / per_block;
+    return static_cast<unsigned>(g < kMaxBwdBlocks ? g : kMaxBwdBlocks);
+}
+
+#define LS_LN_FWD(LPR, NCH, CW)                                                                 \
+    ln_fwd_kernel<LPR, NCH, CW><<<grid, kBlock, 0, st>>>(y16, mean, rstd, x16, g16, b16, r32, h32, eps)
+#define LS_LN_BWD(LPR, NCH, CW)                                                                 \
+    ln_bwd_kernel<LPR, NCH, CW><<<grid, kBlock, lds_bytes, st>>>(dx16, part, dy16, x16, g16, mean, rstd, r32, h32)
+
+#define LS_LN_TABLE(M)                                                                          \
+    if (s.cw == 8) {                                                                            \
+        if (s.lpr == 8) M(8, 1, 8);                                                             \
+        else if (s.lpr == 16 && s.nch == 1) M(16, 1, 8);                                        \
+        else if (s.lpr == 16) M(16, 2, 8);                                                      \
+        else if (s.lpr == 32 && s.nch == 2) M(32, 2, 8);                                        \
+        else if (s.lpr == 32 && s.nch == 3) M(32, 3, 8);                                        \
+        else if (s.lpr == 32) M(32, 4, 8);                                                      \
+        else if (s.nch == 4) M(64, 4, 8);                                                       \
+        else M(64, 8, 8);                                                                       \
+    } else {                                                                                    \
+        switch (s.nch) {                                                                        \
+            case 1: M(64, 1, 1); break;                                                         \
+            case 2: M(64, 2, 1); break;                                                         \
+            case 4: M(64, 4, 1); break;                                                         \
+            case 8: M(64, 8, 1); break;                                                         \
+            case 16: M(64, 16, 1); break;                                                       \
+            case 32: M(64, 32, 1); break;                                                       \
+            default: M(64, 64, 1); break;                                                       \
+        }                                                                                       \
+    }
+
+}  // namespace
+}  // namespace ls
+
+extern "C" {
+
+int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const void* gamma,
+                     const void* beta, int64_t rows, int64_t hidden, float eps, void* stream) {
+    using namespace ls;
+    const char* name = "ls_layernorm_fwd";
+    if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    if (!(eps > 0.0f) || !host_finite(eps)) return fail(LS_ERR_PARAM, "%s: eps must be > 0", name);
+    if (rows == 0) {
+        set_dispatch("empty");
+        return LS_OK;
+    }
+    if (hidden == 0) return fail(LS_ERR_SHAPE, "%s: hidden must be >= 1", name);
+    if (hidden > kMaxHidden)
+        return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
+    if (rows >= (1ll << 32)) return fail(LS_ERR_SHAPE, "%s: too many rows", name);
+    if (!y || !mean || !rstd || !x || !gamma || !beta) return fail(LS_ERR_NULL, "%s: null pointer", name);
+    const bool vec = hidden % 8 == 0 && aligned16(y) && aligned16(x) && aligned16(gamma) && aligned16(beta);
+    LnShape s;
+    ln_shape(hidden, vec, &s);
+    const unsigned grid = fwd_grid(rows, s);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto* y16 = static_cast<half_t*>(y);
+    auto* x16 = static_cast<const half_t*>(x);
+    auto* g16 = static_cast<const half_t*>(gamma);
+    auto* b16 = static_cast<const half_t*>(beta);
+    const uint32_t r32 = static_cast<uint32_t>(rows), h32 = static_cast<uint32_t>(hidden);
+    clear_hip_error();
+    LS_LN_TABLE(LS_LN_FWD)
+    char buf[96];
+    snprintf(buf, sizeof(buf), "layernorm_fwd/%s", s.name);
+    set_dispatch(buf);
+    return launch_status(name);
+}
+
+size_t ls_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
+    if (rows <= 0 || hidden <= 0 || hidden > ls::kMaxHidden) return 0;
+    return static_cast<size_t>(ls::bwd_grid(rows, hidden)) * 2 * static_cast<size_t>(hidden) * sizeof(float);
+}
+
+int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
+                     const void* gamma, const float* mean, const float* rstd, int64_t rows,
+                     int64_t hidden, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace ls;
+    const char* name = "ls_layernorm_bwd";
+    if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    if (rows == 0) {
+        set_dispatch("empty");
+        return LS_OK;   // dgamma / dbeta of zero rows are left untouched
+    }
+    if (hidden == 0) return fail(LS_ERR_SHAPE, "%s: hidden must be >= 1", name);
+    if (hidden > kMaxHidden)
+        return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
+    if (rows >= (1ll << 32)) return fail(LS_ERR_SHAPE, "%s: too many rows", name);
+    if (!dx || !dgamma || !dbeta || !dy || !x || !gamma || !mean || !rstd || !workspace)
+        return fail(LS_ERR_NULL, "%s: null pointer", name);
+    const size_t need = ls_layernorm_bwd_workspace_bytes(rows, hidden);
+    if (workspace_bytes < need)
+        return fail(LS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", name, workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(LS_ERR_PARAM, "%s: workspace must be 16-byte aligned", name);
+    const bool vec = hidden % 8 == 0 && aligned16(dx) && aligned16(dy) && aligned16(x) && aligned16(gamma);
+    LnShape s;
+    ln_shape(hidden, vec, &s);
+    const unsigned grid = bwd_grid(rows, hidden);
+    const size_t lds_bytes = 2 * static_cast<size_t>(hidden) * sizeof(float);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto* dx16 = static_cast<half_t*>(dx);
+    auto* dy16 = static_cast<const half_t*>(dy);
+    auto* x16 = static_cast<const half_t*>(x);
+    auto* g16 = static_cast<const half_t*>(gamma);
+    auto* part = static_cast<float*>(workspace);
+    const uint32_t r32 = static_cast<uint32_t>(rows), h32 = static_cast<uint32_t>(hidden);
+    clear_hip_error();
+    LS_LN_TABLE(LS_LN_BWD)
+    int rc = launch_status(name);
+    if (rc != LS_OK) return rc;
+    const unsigned fgrid = static_cast<unsigned>((hidden + 63) / 64);
+    ln_bwd_finalize_kernel<<<fgrid, kFinSlices * 64, 0, st>>>(static_cast<half_t*>(dgamma),
+                                                               static_cast<half_t*>(dbeta), part,
+                                                               grid, h32);
+    char buf[96];
+    snprintf(buf, sizeof(buf), "layernorm_bwd/%s_g%u", s.name, grid);
+    set_dispatch(buf);
+    return launch_status(name);
+}
+
+}  // extern "C"

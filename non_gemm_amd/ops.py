@@ -1,0 +1,196 @@
+"""Torch-tensor front end of the ls_mi355 C ABI.
+
+Argument marshalling only: every function checks device, dtype, contiguity
+and shapes, passes raw device pointers and the current HIP stream to the
+library, and raises LsError on a non-zero status.  All arithmetic runs in the
+library's HIP kernels; nothing here computes on the host.
+"""
+
+import torch
+
+from ._lib import check, load
+
+_F16 = torch.float16
+_F32 = torch.float32
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _dev(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("ls_mi355 ops take device (cuda/HIP) tensors")
+        if not t.is_contiguous():
+            raise ValueError("ls_mi355 ops take contiguous tensors")
+
+
+def _dtype(t, dt, what):
+    if t.dtype != dt:
+        raise TypeError(f"{what} must be {dt}, got {t.dtype}")
+
+
+def _rows_cols(x):
+    if x.dim() < 1:
+        raise ValueError("need at least one dimension")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    return rows, cols
+
+
+def bias_dropout_residual(x, bias, residual, p, seed, offset, out=None):
+    """out = residual + Dropout(x + bias); x, residual [..., H] fp16, bias [H]."""
+    _dev(x, bias, residual, out)
+    for t, n in ((x, "x"), (bias, "bias"), (residual, "residual")):
+        _dtype(t, _F16, n)
+    if residual.shape != x.shape or bias.shape != (x.shape[-1],):
+        raise ValueError("shape mismatch")
+    out = torch.empty_like(x) if out is None else out
+    rows, cols = _rows_cols(x)
+    check("ls_bias_dropout_residual", load().ls_bias_dropout_residual(
+        _ptr(out), _ptr(x), _ptr(bias), _ptr(residual), rows, cols, float(p), int(seed), int(offset), _stream()))
+    return out
+
+
+def bias_relu_dropout(x, bias, p, seed, offset, out=None):
+    """out = Dropout(ReLU(x + bias)); x [..., F] fp16, bias [F]."""
+    _dev(x, bias, out)
+    _dtype(x, _F16, "x")
+    _dtype(bias, _F16, "bias")
+    if bias.shape != (x.shape[-1],):
+        raise ValueError("shape mismatch")
+    out = torch.empty_like(x) if out is None else out
+    rows, cols = _rows_cols(x)
+    check("ls_bias_relu_dropout", load().ls_bias_relu_dropout(
+        _ptr(out), _ptr(x), _ptr(bias), rows, cols, float(p), int(seed), int(offset), _stream()))
+    return out
+
+
+def layernorm_fwd(x, gamma, beta, eps, y=None, mean=None, rstd=None):
+    """Returns (y fp16, mean fp32 [rows], rstd fp32 [rows])."""
+    _dev(x, gamma, beta, y, mean, rstd)
+    for t, n in ((x, "x"), (gamma, "gamma"), (beta, "beta")):
+        _dtype(t, _F16, n)
+    rows, h = _rows_cols(x)
+    if gamma.shape != (h,) or beta.shape != (h,):
+        raise ValueError("shape mismatch")
+    y = torch.empty_like(x) if y is None else y
+    mean = torch.empty(rows, dtype=_F32, device=x.device) if mean is None else mean
+    rstd = torch.empty(rows, dtype=_F32, device=x.device) if rstd is None else rstd
+    check("ls_layernorm_fwd", load().ls_layernorm_fwd(
+        _ptr(y), _ptr(mean), _ptr(rstd), _ptr(x), _ptr(gamma), _ptr(beta), rows, h, float(eps), _stream()))
+    return y, mean, rstd
+
+
+def layernorm_bwd_workspace_bytes(rows, hidden):
+    return int(load().ls_layernorm_bwd_workspace_bytes(int(rows), int(hidden)))
+
+
+def layernorm_bwd(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None, workspace=None):
+    """Returns (dx fp16, dgamma fp16 [H], dbeta fp16 [H])."""
+    _dev(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace)
+    rows, h = _rows_cols(x)
+    if dy.shape != x.shape or gamma.shape != (h,) or mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("shape mismatch")
+    dx = torch.empty_like(x) if dx is None else dx
+    dgamma = torch.empty(h, dtype=_F16, device=x.device) if dgamma is None else dgamma
+    dbeta = torch.empty(h, dtype=_F16, device=x.device) if dbeta is None else dbeta
+    need = layernorm_bwd_workspace_bytes(rows, h)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    check("ls_layernorm_bwd", load().ls_layernorm_bwd(
+        _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd),
+        rows, h, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return dx, dgamma, dbeta
+
+
+def softmax_fwd(x, key_lengths=None, causal=False, y=None):
+    """x [batch, heads, q_len, k_len] fp16; key_lengths int32 [batch] or None."""
+    _dev(x, key_lengths, y)
+    _dtype(x, _F16, "x")
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, heads, q_len, k_len]")
+    b, h, q, k = x.shape
+    if key_lengths is not None:
+        _dtype(key_lengths, torch.int32, "key_lengths")
+        if key_lengths.numel() != b:
+            raise ValueError("key_lengths must have one entry per sequence")
+    y = torch.empty_like(x) if y is None else y
+    check("ls_softmax_fwd", load().ls_softmax_fwd(
+        _ptr(y), _ptr(x), b, h, q, k, _ptr(key_lengths), int(bool(causal)), _stream()))
+    return y
+
+
+def softmax_bwd(y, dy, dx=None):
+    """dx = y * (dy - sum(y * dy)) over the last axis."""
+    _dev(y, dy, dx)
+    _dtype(y, _F16, "y")
+    _dtype(dy, _F16, "dy")
+    if dy.shape != y.shape:
+        raise ValueError("shape mismatch")
+    dx = torch.empty_like(y) if dx is None else dx
+    rows, k = _rows_cols(y)
+    check("ls_softmax_bwd", load().ls_softmax_bwd(_ptr(dx), _ptr(y), _ptr(dy), rows, k, _stream()))
+    return dx
+
+
+def embedding_fwd(ids, tok_emb, pos_emb, scale, p, seed, offset, out=None):
+    """ids int32 [batch, L]; tok_emb fp16 [V, H]; pos_emb fp16 [max_pos, H]."""
+    _dev(ids, tok_emb, pos_emb, out)
+    _dtype(ids, torch.int32, "ids")
+    _dtype(tok_emb, _F16, "tok_emb")
+    _dtype(pos_emb, _F16, "pos_emb")
+    b, l = ids.shape
+    v, h = tok_emb.shape
+    out = torch.empty((b * l, h), dtype=_F16, device=ids.device) if out is None else out
+    check("ls_embedding_fwd", load().ls_embedding_fwd(
+        _ptr(out), _ptr(ids), _ptr(tok_emb), _ptr(pos_emb), b, l, h, v, pos_emb.shape[0],
+        float(scale), float(p), int(seed), int(offset), _stream()))
+    return out
+
+
+def embedding_bwd(ids, dy, grad_tok_emb, scale, p, seed, offset, zero_first=True):
+    """grad_tok_emb fp32 [V, H] (+)= scale * sum of masked dy rows per id."""
+    _dev(ids, dy, grad_tok_emb)
+    _dtype(ids, torch.int32, "ids")
+    _dtype(dy, _F16, "dy")
+    _dtype(grad_tok_emb, _F32, "grad_tok_emb")
+    b, l = ids.shape
+    v, h = grad_tok_emb.shape
+    if dy.numel() != b * l * h:
+        raise ValueError("dy must be [batch * L, H]")
+    check("ls_embedding_bwd", load().ls_embedding_bwd(
+        _ptr(grad_tok_emb), _ptr(ids), _ptr(dy), b, l, h, v, float(scale), float(p), int(seed),
+        int(offset), int(bool(zero_first)), _stream()))
+    return grad_tok_emb
+
+
+def adam_workspace_step(param, grad, exp_avg, exp_avg_sq, lr, beta1, beta2, eps, weight_decay,
+                        step, grad_scale=1.0, decoupled_wd=True):
+    """One in-place Adam step over flat fp16 param/grad and fp32 moments."""
+    _dev(param, grad, exp_avg, exp_avg_sq)
+    _dtype(param, _F16, "param")
+    _dtype(grad, _F16, "grad")
+    _dtype(exp_avg, _F32, "exp_avg")
+    _dtype(exp_avg_sq, _F32, "exp_avg_sq")
+    n = param.numel()
+    if grad.numel() != n or exp_avg.numel() != n or exp_avg_sq.numel() != n:
+        raise ValueError("workspace tensors must have equal length")
+    check("ls_adam_workspace_step", load().ls_adam_workspace_step(
+        _ptr(param), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n, float(lr), float(beta1),
+        float(beta2), float(eps), float(weight_decay), int(step), float(grad_scale),
+        int(bool(decoupled_wd)), _stream()))
+
+
+def dropout_mask(n, p, seed, offset, device="cuda"):
+    """uint8 [n]: 1 where the dropout kernels keep element i, 0 where they drop it."""
+    keep = torch.empty(int(n), dtype=torch.uint8, device=device)
+    check("ls_dropout_mask", load().ls_dropout_mask(_ptr(keep), int(n), float(p), int(seed), int(offset), _stream()))
+    return keep

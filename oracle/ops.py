@@ -211,7 +211,9 @@ def softmax_fwd(x, key_lengths=None, causal=False):
     valid = softmax_valid(b, h, q, k, key_lengths, causal)
     masked = np.where(valid, x64, -np.inf)
     m = masked.max(axis=-1, keepdims=True)
-    m = np.where(np.isfinite(m), m, 0.0)
+    # A row whose valid entries are all -inf (or that has none) normalises to
+    # zeros; +inf or NaN inputs give NaN rows, as exp(x - m) / sum does.
+    m = np.where(m == -np.inf, 0.0, m)
     e = np.where(valid, np.exp(masked - m), 0.0)
     s = e.sum(axis=-1, keepdims=True)
     y = np.divide(e, s, out=np.zeros_like(e), where=s > 0)

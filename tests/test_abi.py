@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is ever launched).
+
+The library must load, export every function include/ls_mi355.h declares,
+and reject invalid arguments with the documented status before touching the
+GPU.  Every call below fails validation, so no HIP work is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from non_gemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ls_mi355.h")
+
+LS_OK, LS_ERR_NULL, LS_ERR_SHAPE, LS_ERR_PARAM, LS_ERR_WORKSPACE, LS_ERR_UNSUPPORTED = 0, 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ls_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from non_gemm_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_introspection(lib):
+    assert lib.ls_dropout_decision_bits() == 16
+    assert lib.ls_version().decode().startswith("ls_mi355")
+    assert lib.ls_status_string(LS_ERR_WORKSPACE).decode() == "workspace too small"
+    assert lib.ls_status_string(99).decode() == "unknown status"
+
+
+def test_elementwise_validation(lib):
+    s = None
+    assert lib.ls_bias_dropout_residual(FAKE, FAKE, FAKE, FAKE, -1, 8, 0.1, 1, 0, s) == LS_ERR_SHAPE
+    assert lib.ls_bias_dropout_residual(FAKE, FAKE, FAKE, FAKE, 4, 8, 1.5, 1, 0, s) == LS_ERR_PARAM
+    assert lib.ls_bias_dropout_residual(FAKE, FAKE, FAKE, FAKE, 4, 8, float("nan"), 1, 0, s) == LS_ERR_PARAM
+    assert lib.ls_bias_dropout_residual(FAKE, None, FAKE, FAKE, 4, 8, 0.1, 1, 0, s) == LS_ERR_NULL
+    assert b"null" in lib.ls_last_error()
+    assert lib.ls_bias_relu_dropout(FAKE, FAKE, None, 4, 8, 0.1, 1, 0, s) == LS_ERR_NULL
+    assert lib.ls_bias_relu_dropout(FAKE, FAKE, FAKE, 4, 8, -0.1, 1, 0, s) == LS_ERR_PARAM
+    # empty tensors are valid no-ops, NULL pointers allowed
+    assert lib.ls_bias_relu_dropout(None, None, None, 0, 8, 0.1, 1, 0, s) == LS_OK
+    assert lib.ls_last_dispatch() == b"empty"
+    assert lib.ls_dropout_mask(None, 0, 0.5, 1, 0, s) == LS_OK
+    assert lib.ls_dropout_mask(None, 10, 0.5, 1, 0, s) == LS_ERR_NULL
+    assert lib.ls_dropout_mask(FAKE, -1, 0.5, 1, 0, s) == LS_ERR_SHAPE
+
+
+def test_layernorm_validation(lib):
+    s = None
+    assert lib.ls_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 0.0, s) == LS_ERR_PARAM
+    assert lib.ls_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0, 1e-5, s) == LS_ERR_SHAPE
+    assert lib.ls_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8192, 1e-5, s) == LS_ERR_UNSUPPORTED
+    assert lib.ls_layernorm_fwd(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 1e-5, s) == LS_ERR_NULL
+    assert lib.ls_layernorm_fwd(None, None, None, None, None, None, 0, 8, 1e-5, s) == LS_OK
+    need = lib.ls_layernorm_bwd_workspace_bytes(4096, 768)
+    assert need > 0 and need % (2 * 768 * 4) == 0
+    assert lib.ls_layernorm_bwd_workspace_bytes(0, 768) == 0
+    assert lib.ls_layernorm_bwd_workspace_bytes(10, 5000) == 0
+    assert lib.ls_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 768,
+                                FAKE, need - 1, s) == LS_ERR_WORKSPACE
+    assert lib.ls_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 768,
+                                None, need, s) == LS_ERR_NULL
+    assert lib.ls_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 768,
+                                ctypes.c_void_p(0x1008), need, s) == LS_ERR_PARAM
+
+
+def test_softmax_validation(lib):
+    s = None
+    assert lib.ls_softmax_fwd(FAKE, FAKE, 2, 2, 4, -1, None, 0, s) == LS_ERR_SHAPE
+    assert lib.ls_softmax_fwd(FAKE, FAKE, 1, 1, 1, 65544, None, 0, s) == LS_ERR_UNSUPPORTED
+    assert lib.ls_softmax_fwd(FAKE, FAKE, 1, 1, 1, 1030, None, 0, s) == LS_ERR_UNSUPPORTED   # element-wise path limit
+    assert lib.ls_softmax_fwd(None, FAKE, 1, 1, 1, 128, None, 0, s) == LS_ERR_NULL
+    assert lib.ls_softmax_fwd(FAKE, FAKE, 1 << 20, 1 << 10, 1 << 10, 128, None, 0, s) == LS_ERR_SHAPE
+    assert lib.ls_softmax_fwd(None, None, 0, 12, 128, 128, None, 1, s) == LS_OK
+    assert lib.ls_softmax_bwd(FAKE, None, FAKE, 4, 128, s) == LS_ERR_NULL
+    assert lib.ls_softmax_bwd(None, None, None, 0, 128, s) == LS_OK
+
+
+def test_embedding_validation(lib):
+    s = None
+    assert lib.ls_embedding_fwd(FAKE, FAKE, FAKE, FAKE, 2, 16, 8, 10, 8, 1.0, 0.1, 1, 0, s) == LS_ERR_SHAPE
+    assert lib.ls_embedding_fwd(FAKE, FAKE, FAKE, FAKE, 2, 16, 8, 10, 16, 1.0, 2.0, 1, 0, s) == LS_ERR_PARAM
+    assert lib.ls_embedding_fwd(FAKE, FAKE, FAKE, FAKE, 2, 16, 8, 10, 16, float("inf"), 0.1, 1, 0, s) == LS_ERR_PARAM
+    assert lib.ls_embedding_fwd(FAKE, None, FAKE, FAKE, 2, 16, 8, 10, 16, 1.0, 0.1, 1, 0, s) == LS_ERR_NULL
+    assert lib.ls_embedding_bwd(None, FAKE, FAKE, 2, 16, 8, 10, 1.0, 0.1, 1, 0, 1, s) == LS_ERR_NULL
+    assert lib.ls_embedding_bwd(FAKE, FAKE, FAKE, -2, 16, 8, 10, 1.0, 0.1, 1, 0, 1, s) == LS_ERR_SHAPE
+    assert lib.ls_embedding_bwd(None, None, None, 0, 16, 8, 0, 1.0, 0.1, 1, 0, 1, s) == LS_OK
+
+
+def test_adam_validation(lib):
+    s = None
+    a = (FAKE, FAKE, FAKE, FAKE, 100)
+    assert lib.ls_adam_workspace_step(*a, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, 1.0, 1, s) == LS_ERR_PARAM
+    assert lib.ls_adam_workspace_step(*a, 1e-3, 1.0, 0.999, 1e-8, 0.0, 1, 1.0, 1, s) == LS_ERR_PARAM
+    assert lib.ls_adam_workspace_step(*a, 1e-3, 0.9, 0.999, 0.0, 0.0, 1, 1.0, 1, s) == LS_ERR_PARAM
+    assert lib.ls_adam_workspace_step(*a, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0.0, 1, s) == LS_ERR_PARAM
+    assert lib.ls_adam_workspace_step(*a, -1.0, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 1, s) == LS_ERR_PARAM
+    assert lib.ls_adam_workspace_step(FAKE, None, FAKE, FAKE, 100, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 1, s) == LS_ERR_NULL
+    assert lib.ls_adam_workspace_step(None, None, None, None, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 1, s) == LS_OK

@@ -1,0 +1,418 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by element.
+
+Bars (written here, not in the oracle):
+* dropout masks, argmax and indexing: bit-exact;
+* fp16 outputs: an element fails iff |a-b| > 2e-3 and |a-b| > 1e-2 |b|;
+* fp32 statistics and moments: |a-b| <= 1e-5 * max(|b|, floor).
+Shapes cover several tiles, ragged tails, the vector and element-wise paths,
+the empty case and the workloads' full sizes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from conftest import fp16_mismatch
+
+pytestmark = pytest.mark.gpu
+
+BITS = 16
+SEED = synth.DROPOUT_SEED
+
+
+@pytest.fixture(scope="module")
+def ls():
+    from non_gemm_amd import _lib, ops
+    _lib.load()
+    assert _lib.dropout_decision_bits() == BITS
+    return ops
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_fp16(a, b, what):
+    bad = fp16_mismatch(a, b)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} out of tolerance; first at {i}: "
+                             f"{np.asarray(a)[i]} vs oracle {np.asarray(b)[i]}")
+
+
+def assert_fp32(a, b, what, floor=1e-30):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    tol = 1e-5 * np.maximum(np.abs(b), floor)
+    bad = ~(np.abs(a - b) <= tol)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} out of tolerance; first at {i}: "
+                             f"{a[i]} vs oracle {b[i]}")
+
+
+def last_dispatch():
+    from non_gemm_amd import _lib
+    return _lib.last_dispatch()
+
+
+# ----------------------------------------------------------------------------
+# Dropout mask
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,p,seed,offset", [
+    (1, 0.1, SEED, 0),
+    (1_000_003, 0.1, SEED, 0),
+    (65_541, 0.5, 7, 3),
+    (4096 * 768, 0.1, SEED, 2),
+    (12_345, 0.0, 1, 1),
+    (12_345, 1.0, 1, 1),
+    (999, 0.999, 2**64 - 1, 2**64 - 1),
+])
+def test_dropout_mask_bit_exact(ls, n, p, seed, offset):
+    keep = host(ls.dropout_mask(n, p, seed, offset)).astype(bool)
+    ref = oracle.dropout_keep(n, p, seed, offset, BITS)
+    assert keep.shape == ref.shape
+    assert np.array_equal(keep, ref), f"{int((keep != ref).sum())} decisions differ"
+
+
+# ----------------------------------------------------------------------------
+# bias + dropout + residual / bias + ReLU + dropout
+# ----------------------------------------------------------------------------
+
+EW_SHAPES = [(128, 256), (4096, 768), (37, 24), (5, 1000), (3, 13), (1, 8), (0, 64)]
+
+
+@pytest.mark.parametrize("rows,cols", EW_SHAPES)
+@pytest.mark.parametrize("p", [0.1, 0.0])
+def test_bias_dropout_residual(ls, rows, cols, p):
+    g = np.random.default_rng(rows * 1000 + cols)
+    x = synth.normal16(g, (rows, cols), 1.0)
+    r = synth.normal16(g, (rows, cols), 1.0)
+    b = synth.normal16(g, (cols,), 0.02)
+    out = host(ls.bias_dropout_residual(dev(x), dev(b), dev(r), p, SEED, synth.SITE_ATTN_OUT))
+    ref = oracle.bias_dropout_residual(x, b, r, p, SEED, synth.SITE_ATTN_OUT, BITS)
+    assert_fp16(out, ref, f"bias_dropout_residual {rows}x{cols} p={p} [{last_dispatch()}]")
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 256), (333, 40), (7, 13)])
+def test_bias_dropout_residual_mask_exposed(ls, rows, cols):
+    """x = 1, b = 0, r = 0: the output is exactly the mask times the scale."""
+    x = np.ones((rows, cols), np.float16)
+    z = np.zeros((rows, cols), np.float16)
+    out = host(ls.bias_dropout_residual(dev(x), dev(np.zeros(cols, np.float16)), dev(z), 0.25, 11, 4))
+    keep = oracle.dropout_keep(rows * cols, 0.25, 11, 4, BITS).reshape(rows, cols)
+    assert np.array_equal(out != 0, keep)
+    assert np.all(out[keep] == np.float16(1 / 0.75))
+
+
+def test_bias_dropout_residual_aliasing_and_unaligned(ls):
+    g = np.random.default_rng(5)
+    rows, cols = 300, 64
+    x = synth.normal16(g, (rows, cols), 1.0)
+    r = synth.normal16(g, (rows, cols), 1.0)
+    b = synth.normal16(g, (cols,), 0.02)
+    ref = oracle.bias_dropout_residual(x, b, r, 0.1, SEED, 0, BITS)
+    rt = dev(r)
+    ls.bias_dropout_residual(dev(x), dev(b), rt, 0.1, SEED, 0, out=rt)      # out aliases residual
+    assert_fp16(host(rt), ref, "aliased out=residual")
+    # unaligned views (offset by one element) take the element-wise path
+    big = torch.empty(rows * cols + 1, dtype=torch.float16, device="cuda")
+    xv = big[1:].view(rows, cols)
+    xv.copy_(dev(x))
+    out = host(ls.bias_dropout_residual(xv, dev(b), dev(r), 0.1, SEED, 0))
+    assert "scalar" in last_dispatch()
+    assert_fp16(out, ref, "unaligned x")
+
+
+@pytest.mark.parametrize("rows,cols", [(4096, 3072), (128, 1024), (37, 24), (5, 1000), (3, 13), (0, 8)])
+@pytest.mark.parametrize("p", [0.1, 0.0, 1.0])
+def test_bias_relu_dropout(ls, rows, cols, p):
+    g = np.random.default_rng(rows * 7 + cols)
+    x = synth.normal16(g, (rows, cols), 1.0)
+    b = synth.normal16(g, (cols,), 0.02)
+    out = host(ls.bias_relu_dropout(dev(x), dev(b), p, SEED, synth.SITE_FFN_ACT))
+    ref = oracle.bias_relu_dropout(x, b, p, SEED, synth.SITE_FFN_ACT, BITS)
+    assert_fp16(out, ref, f"bias_relu_dropout {rows}x{cols} p={p} [{last_dispatch()}]")
+
+
+def test_nan_inf_propagate(ls):
+    x = np.array([[np.nan, np.inf, -np.inf, 1.0, -1.0, 0.0, 2.0, 3.0]], np.float16)
+    b = np.zeros(8, np.float16)
+    out = host(ls.bias_relu_dropout(dev(x), dev(b), 0.0, 1, 0))
+    ref = oracle.bias_relu_dropout(x, b, 0.0, 1, 0, BITS)
+    assert_fp16(out, ref, "relu nan/inf")
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm
+# ----------------------------------------------------------------------------
+
+LN_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (1000, 64), (77, 96), (33, 512), (9, 1536),
+             (5, 2048), (3, 4096), (50, 100), (20, 13), (1, 8), (300, 768)]
+
+
+def ln_inputs(rows, h, seed):
+    g = np.random.default_rng(seed)
+    return (synth.normal16(g, (rows, h), 1.0), synth.uniform16(g, (h,), 0.5, 1.5),
+            synth.normal16(g, (h,), 0.1), synth.normal16(g, (rows, h), 1.0))
+
+
+@pytest.mark.parametrize("rows,h", LN_SHAPES)
+def test_layernorm_fwd(ls, rows, h):
+    x, gamma, beta, _ = ln_inputs(rows, h, rows + h)
+    y, mean, rstd = ls.layernorm_fwd(dev(x), dev(gamma), dev(beta), synth.LN_EPS)
+    ry, rmean, rrstd = oracle.layernorm_fwd(x, gamma, beta, synth.LN_EPS)
+    tag = f"layernorm_fwd {rows}x{h} [{last_dispatch()}]"
+    assert_fp16(host(y), ry, tag)
+    sigma = 1.0 / rrstd.astype(np.float64)
+    assert_fp32(host(mean), rmean, tag + " mean", floor=sigma)
+    assert_fp32(host(rstd), rrstd, tag + " rstd")
+
+
+@pytest.mark.parametrize("rows,h", LN_SHAPES)
+def test_layernorm_bwd(ls, rows, h):
+    x, gamma, beta, dy = ln_inputs(rows, h, rows * 3 + h)
+    _, mean, rstd = oracle.layernorm_fwd(x, gamma, beta, synth.LN_EPS)
+    dx, dg, db = ls.layernorm_bwd(dev(dy), dev(x), dev(gamma), dev(mean), dev(rstd))
+    rdx, rdg, rdb = oracle.layernorm_bwd(dy, x, gamma, mean, rstd)
+    tag = f"layernorm_bwd {rows}x{h} [{last_dispatch()}]"
+    assert_fp16(host(dx), rdx, tag + " dx")
+    assert_fp16(host(dg), rdg, tag + " dgamma")
+    assert_fp16(host(db), rdb, tag + " dbeta")
+    # the column reduction has a fixed order: a second run is bit-identical
+    dx2, dg2, db2 = ls.layernorm_bwd(dev(dy), dev(x), dev(gamma), dev(mean), dev(rstd))
+    assert np.array_equal(host(dg2), host(dg)) and np.array_equal(host(db2), host(db))
+    assert np.array_equal(host(dx2), host(dx))
+
+
+def test_layernorm_degenerate_rows(ls):
+    """Constant rows give y = beta; rows (+a, -a, ...) the closed form."""
+    h = 256
+    x = np.zeros((4, h), np.float16)
+    x[0] = 3.0
+    x[1] = np.tile([0.5, -0.5], h // 2)
+    x[2] = np.tile([100.0, -100.0], h // 2)
+    gamma = np.ones(h, np.float16)
+    beta = np.full(h, 0.25, np.float16)
+    y, mean, rstd = ls.layernorm_fwd(dev(x), dev(gamma), dev(beta), synth.LN_EPS)
+    ry, _, rrstd = oracle.layernorm_fwd(x, gamma, beta, synth.LN_EPS)
+    assert_fp16(host(y), ry, "degenerate rows")
+    assert np.all(host(y)[0] == np.float16(0.25)) and np.all(host(y)[3] == np.float16(0.25))
+
+
+# ----------------------------------------------------------------------------
+# Softmax
+# ----------------------------------------------------------------------------
+
+SM_SHAPES = [(8, 12, 128, 128), (32, 12, 128, 128), (32, 16, 256, 256), (2, 3, 17, 64),
+             (2, 2, 9, 512), (1, 2, 5, 1024), (1, 1, 3, 2048), (1, 1, 3, 4096), (1, 2, 2, 8192),
+             (1, 1, 2, 20000), (2, 2, 7, 100), (2, 3, 5, 7), (1, 1, 1, 1), (0, 12, 128, 128)]
+
+
+@pytest.mark.parametrize("shape", SM_SHAPES)
+def test_softmax_fwd_dense(ls, shape):
+    g = np.random.default_rng(sum(shape))
+    x = synth.normal16(g, shape, 3.0)
+    y = host(ls.softmax_fwd(dev(x)))
+    ref = oracle.softmax_fwd(x)
+    tag = f"softmax_fwd {shape} [{last_dispatch()}]"
+    assert_fp16(y, ref, tag)
+    if x.size:
+        # argmax: compare where the oracle's row maximum is unique
+        r = ref.reshape(-1, shape[-1]).astype(np.float64)
+        yy = y.reshape(-1, shape[-1]).astype(np.float64)
+        top = r.max(1, keepdims=True)
+        unique = (r == top).sum(1) == 1
+        assert np.array_equal(np.argmax(yy[unique], 1), np.argmax(r[unique], 1)), tag
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("with_lengths", [True, False])
+def test_softmax_fwd_c2_masked(ls, causal, with_lengths):
+    inp = synth.softmax_inputs()
+    x, lens = inp["scores"], inp["key_lengths"]
+    if not with_lengths and not causal:
+        pytest.skip("dense case covered above")
+    kl = lens if with_lengths else None
+    y = host(ls.softmax_fwd(dev(x), dev(kl) if kl is not None else None, causal))
+    ref = oracle.softmax_fwd(x, kl, causal)
+    tag = f"softmax_fwd C2 causal={causal} lengths={with_lengths} [{last_dispatch()}]"
+    assert_fp16(y, ref, tag)
+    valid = oracle.ops.softmax_valid(*x.shape, kl, causal)
+    assert np.all(y[~valid] == 0), tag + ": masked entries must be exactly 0"
+
+
+@pytest.mark.parametrize("k", [64, 100, 128, 4096, 8192])
+def test_softmax_fwd_edge_lengths(ls, k):
+    """Key lengths 0, 1, ragged and beyond k (clamped); causal rows."""
+    g = np.random.default_rng(k)
+    b = 6
+    x = synth.normal16(g, (b, 2, 5, k), 3.0)
+    lens = np.array([0, 1, k // 2 + 3, k, k + 10, -4], np.int32)
+    for causal in (False, True):
+        y = host(ls.softmax_fwd(dev(x), dev(lens), causal))
+        ref = oracle.softmax_fwd(x, lens, causal)
+        assert_fp16(y, ref, f"softmax_fwd k={k} causal={causal} [{last_dispatch()}]")
+        assert np.all(y[0] == 0) and np.all(y[5] == 0)
+
+
+@pytest.mark.parametrize("shape", SM_SHAPES)
+def test_softmax_bwd(ls, shape):
+    g = np.random.default_rng(sum(shape) + 1)
+    x = synth.normal16(g, shape, 3.0)
+    yv = oracle.softmax_fwd(x)
+    dy = synth.normal16(g, shape, 1.0)
+    k = shape[-1]
+    dx = host(ls.softmax_bwd(dev(yv), dev(dy)))
+    ref = oracle.softmax_bwd(yv.reshape(-1, k), dy.reshape(-1, k)).reshape(shape)
+    assert_fp16(dx, ref, f"softmax_bwd {shape} [{last_dispatch()}]")
+
+
+def test_softmax_bwd_c2_masked_and_alias(ls):
+    inp = synth.softmax_inputs()
+    yv = oracle.softmax_fwd(inp["scores"], inp["key_lengths"], True)
+    dy = inp["grad_out"]
+    k = yv.shape[-1]
+    dyt = dev(dy)
+    ls.softmax_bwd(dev(yv), dyt, dx=dyt)          # dx aliases dy
+    ref = oracle.softmax_bwd(yv.reshape(-1, k), dy.reshape(-1, k)).reshape(yv.shape)
+    out = host(dyt)
+    assert_fp16(out, ref, "softmax_bwd C2 aliased")
+    assert np.all(out[yv == 0] == 0)
+
+
+# ----------------------------------------------------------------------------
+# Embedding
+# ----------------------------------------------------------------------------
+
+def test_embedding_c4(ls):
+    inp = synth.embedding_inputs()
+    ids, E, P, s = inp["ids"], inp["tok_emb"], inp["pos_emb"], inp["scale"]
+    p, off = synth.DROPOUT_P, synth.SITE_EMBEDDING
+    out = host(ls.embedding_fwd(dev(ids), dev(E), dev(P), s, p, SEED, off))
+    ref = oracle.embedding_fwd(ids, E, P, s, p, SEED, off, BITS)
+    assert_fp16(out, ref, f"embedding_fwd C4 [{last_dispatch()}]")
+    v, h = E.shape
+    dE = torch.full((v, h), 7.0, dtype=torch.float32, device="cuda")     # zero_first must clear it
+    ls.embedding_bwd(dev(ids), dev(inp["grad_out"]), dE, s, p, SEED, off, zero_first=True)
+    got = host(dE)
+    want = oracle.embedding_bwd(ids, inp["grad_out"], v, s, p, SEED, off, BITS)
+    # fp32 atomics sum in no fixed order: bound by 1e-5 of the sum of |terms|
+    keep = oracle.dropout_keep(ids.size * h, p, SEED, off, BITS).reshape(-1, h)
+    terms = np.abs(s * inp["grad_out"].astype(np.float64) * keep * oracle.dropout_scale(p, BITS))
+    mag = np.zeros((v, h))
+    np.add.at(mag, ids.reshape(-1), terms)
+    err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    assert np.all(err <= 1e-5 * mag + 1e-30), f"embedding_bwd [{last_dispatch()}]: max err {err.max()}"
+    untouched = np.setdiff1d(np.arange(v), ids)
+    assert np.all(got[untouched] == 0)
+
+
+@pytest.mark.parametrize("b,l,h,v", [(2, 7, 64, 50), (3, 5, 768, 100), (1, 33, 24, 9), (2, 4, 20, 11),
+                                     (4, 16, 1024, 3), (1, 1, 8, 1), (1, 40, 2048, 64)])
+def test_embedding_small(ls, b, l, h, v):
+    g = np.random.default_rng(b * l * h)
+    ids = g.integers(0, v, size=(b, l)).astype(np.int32)
+    E = synth.normal16(g, (v, h), 0.2)
+    P = synth.normal16(g, (l + 2, h), 0.5)
+    dy = synth.normal16(g, (b * l, h), 1.0)
+    for p in (0.1, 0.0):
+        out = host(ls.embedding_fwd(dev(ids), dev(E), dev(P), 4.0, p, 9, 3))
+        assert_fp16(out, oracle.embedding_fwd(ids, E, P, 4.0, p, 9, 3, BITS), f"embedding_fwd {b,l,h,v} p={p}")
+        acc = synth.normal16(g, (v, h), 1.0).astype(np.float32)
+        dE = dev(acc.copy())
+        ls.embedding_bwd(dev(ids), dev(dy), dE, 4.0, p, 9, 3, zero_first=False)     # accumulate
+        want = oracle.embedding_bwd(ids, dy, v, 4.0, p, 9, 3, BITS, grad_in=acc)
+        np.testing.assert_allclose(host(dE), want, rtol=1e-5, atol=1e-4,
+                                   err_msg=f"embedding_bwd {b,l,h,v} p={p} [{last_dispatch()}]")
+
+
+def test_embedding_invalid_ids(ls):
+    v, h = 10, 64
+    ids = np.array([[0, 10, -1, 9, 3, 1000]], np.int32)
+    E = np.ones((v, h), np.float16)
+    P = np.zeros((6, h), np.float16)
+    out = host(ls.embedding_fwd(dev(ids), dev(E), dev(P), 1.0, 0.0, 1, 0))
+    assert np.all(np.isnan(out[[1, 2, 5]])) and np.all(out[[0, 3, 4]] == 1)
+    dy = np.ones((6, h), np.float16)
+    dE = torch.zeros((v, h), dtype=torch.float32, device="cuda")
+    ls.embedding_bwd(dev(ids), dev(dy), dE, 1.0, 0.0, 1, 0, zero_first=True)
+    got = host(dE)
+    assert np.all(got[[0, 3, 9]] == 1) and np.all(got[[1, 2, 4, 5, 6, 7, 8]] == 0)
+
+
+# ----------------------------------------------------------------------------
+# Adam over the workspace
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,decoupled,offset,steps", [(1_000_003, True, 0, 10), (77, True, 0, 10),
+                                                      (50_001, True, 3, 10), (4096, False, 0, 1),
+                                                      (4096, False, 0, 10)])
+def test_adam_steps(ls, n, decoupled, offset, steps):
+    """AdamW (the workspace trainer's mode): moments depend on the gradient
+    only, so they meet the fp32 bar over all ten steps.  L2 mode feeds the
+    fp16 parameter back into the gradient; once a parameter's fp16 rounding
+    differs by one ulp between fp32 and fp64 arithmetic, its moments differ by
+    up to wd * ulp, so after the first step only the parameter is compared."""
+    g = np.random.default_rng(n)
+    p = synth.normal16(g, (n,), 0.02)
+    gr = synth.normal16(g, (n,), 1e-3)
+    hp = dict(synth.ADAM_HYPER)
+    hp["decoupled_wd"] = decoupled
+    # offset > 0: views that are not 16-byte aligned take the element-wise path
+    pt = torch.empty(n + offset, dtype=torch.float16, device="cuda")[offset:]
+    pt.copy_(dev(p))
+    gt = dev(gr)
+    mt = torch.zeros(n + offset, dtype=torch.float32, device="cuda")[offset:]
+    vt = torch.zeros(n + offset, dtype=torch.float32, device="cuda")[offset:]
+    rp, rm, rv = p, np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for step in range(1, steps + 1):
+        ls.adam_workspace_step(pt, gt, mt, vt, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                               hp["weight_decay"], step, hp["grad_scale"], decoupled)
+        rp, rm, rv = oracle.adam_workspace_step(rp, gr, rm, rv, hp["lr"], hp["beta1"], hp["beta2"],
+                                                hp["eps"], hp["weight_decay"], step, hp["grad_scale"],
+                                                decoupled)
+    tag = f"adam n={n} steps={steps} [{last_dispatch()}]"
+    assert_fp16(host(pt), rp, tag + " param")
+    if decoupled or steps == 1:
+        assert_fp32(host(mt), rm, tag + " exp_avg")
+        assert_fp32(host(vt), rv, tag + " exp_avg_sq")
+
+
+def test_adam_resume_bit_identical(ls):
+    """5 steps, save, reload, 5 more == 10 straight steps, bit for bit."""
+    from non_gemm_amd import workspace
+    g = np.random.default_rng(3)
+    shapes = [(768, 768), (768,), (3072, 768), (13,)]
+    base = [synth.normal16(g, s, 0.02) for s in shapes]
+    grads = [synth.normal16(g, s, 1e-3) for s in shapes]
+
+    def make():
+        ps = [torch.nn.Parameter(dev(b.copy())) for b in base]
+        ws = workspace.link(ps)
+        for pp, gg in zip(ps, grads):
+            pp.grad.copy_(dev(gg))
+        return ps, ws
+    hp = dict(lr=1e-4, betas=(0.9, 0.98), eps=1e-8, weight_decay=0.01)
+    ps1, ws1 = make()
+    for _ in range(10):
+        ws1.step(**hp)
+    ps2, ws2 = make()
+    for _ in range(5):
+        ws2.step(**hp)
+    state = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in ws2.state_dict().items()}
+    ps3, ws3 = make()
+    ws3.load_state_dict({k: (v.cuda() if torch.is_tensor(v) else v) for k, v in state.items()})
+    for _ in range(5):
+        ws3.step(**hp)
+    assert torch.equal(ws1.param, ws3.param)
+    assert torch.equal(ws1.exp_avg, ws3.exp_avg) and torch.equal(ws1.exp_avg_sq, ws3.exp_avg_sq)
+    # parameters are views of the workspace
+    assert torch.equal(ps3[2].detach().reshape(-1), ws3.param[ws3.offsets[2]:ws3.offsets[2] + 3072 * 768])
