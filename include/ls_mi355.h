@@ -150,14 +150,15 @@ int ls_embedding_fwd(void* out, const int32_t* ids, const void* tok_emb, const v
 
 /* Embedding backward ([LS2] sec. 2.1.2): for every token t with id w,
  *     grad_tok_emb[w, c] += scale * keep(t*hidden + c) / (1-p_eff) * dy[t, c]
- * accumulated with fp32 atomic adds (repeated ids collide on one row), after
- * duplicate ids inside each block of tokens have been summed in registers.
+ * Repeated ids collide on one row of the table; the collisions are summed
+ * with fp32 atomic adds, after the repeats inside each chunk of 64 tokens
+ * have been added up in registers.  The atomics' order is not fixed, so two
+ * runs agree to fp32 rounding, not bit for bit.
  * grad_tok_emb: fp32 [vocab, hidden]; if zero_first != 0 it is zeroed first
  * (by a fill kernel on the same stream), otherwise the call accumulates.
  * dy: fp16 [batch*seq_len, hidden].  (seed, offset, p) must be those of the
- * forward.  Ids outside [0, vocab) contribute nothing.  The summation order
- * of the atomics is not fixed, so results agree to fp32 rounding, not bit
- * for bit, between runs. */
+ * forward.  Ids outside [0, vocab) contribute nothing.  One kernel launch
+ * (two with zero_first). */
 int ls_embedding_bwd(float* grad_tok_emb, const int32_t* ids, const void* dy, int64_t batch,
                      int64_t seq_len, int64_t hidden, int64_t vocab, float scale, float p,
                      uint64_t seed, uint64_t offset, int zero_first, void* stream);

@@ -115,7 +115,7 @@ int launch_elementwise(const char* name, void* out, const void* x, const void* b
                      (!RESID || aligned16(res)) && (n / 8) < (1ull << 31) &&
                      static_cast<uint64_t>(cols / 8) < (1ull << 31);
     if (vec) {
-        constexpr int VPT = 4;
+        constexpr int VPT = 1;
         const uint32_t nvec = static_cast<uint32_t>(n / 8);
         const FastDiv cv(static_cast<uint32_t>(cols / 8));
         const unsigned grid = grid_for(nvec, kBlock * VPT, 1u << 30);
@@ -127,8 +127,8 @@ int launch_elementwise(const char* name, void* out, const void* x, const void* b
             elementwise_vec_kernel<RESID, RELU, true, VPT><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
         else
             elementwise_vec_kernel<RESID, RELU, false, VPT><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
-        set_dispatch(drop ? (RESID ? "bias_dropout_residual/vec8_vpt4" : "bias_relu_dropout/vec8_vpt4")
-                          : (RESID ? "bias_dropout_residual/vec8_vpt4_p0" : "bias_relu_dropout/vec8_vpt4_p0"));
+        set_dispatch(drop ? (RESID ? "bias_dropout_residual/vec8_vpt1" : "bias_relu_dropout/vec8_vpt1")
+                          : (RESID ? "bias_dropout_residual/vec8_vpt1_p0" : "bias_relu_dropout/vec8_vpt1_p0"));
     } else {
         const unsigned grid = grid_for(n, kBlock, 65536);
         auto* o = static_cast<half_t*>(out);

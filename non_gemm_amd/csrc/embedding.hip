@@ -5,13 +5,9 @@
 //
 // Backward: dE[w] += s * sum_{t: id_t = w} m_t * dy_t with the dropout mask
 // m regenerated from (seed, offset).  Repeated ids collide on one row of dE,
-// so the sum is accumulated with fp32 atomic adds.  Each wave first takes a
-// chunk of 16 consecutive tokens, sorts their ids inside the wave (bitonic
-// network over lane shuffles), and walks the tokens in id order, adding the
-// rows of equal ids in registers; only one atomic per (distinct id, column)
-// of the chunk reaches memory.  With Zipf-distributed ids the frequent ids
-// repeat inside a chunk, which cuts the atomic count and the contention on
-// the hottest rows.
+// and, as in [LS2] sec. 2.1.2, the collisions are summed with fp32 atomic
+// adds -- after each wave has added up the repeats inside its own chunk of
+// tokens, and with every atomic instruction covering 64 consecutive floats.
 #include "ls_common.hpp"
 
 namespace ls {
@@ -107,7 +103,19 @@ __global__ __launch_bounds__(kBlock) void emb_fwd_scalar_kernel(half_t* out, con
 // ---------------------------------------------------------------------------
 // Backward
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 16;          // tokens per wave
+// A wave takes a chunk of 64 consecutive tokens and one slice of 512 columns
+// (lane l owns the 8 consecutive columns 8l..8l+7 of the slice, so its dy
+// loads are 16 bytes and one Philox call gives its 8 dropout decisions).
+// The chunk's ids are sorted inside the wave (bitonic network over lane
+// shuffles), so the tokens of one id arrive back to back and are summed in
+// registers.  At the end of each run of equal ids the wave writes its sum
+// to LDS and reads it back transposed -- lane l then holds columns l, l+64,
+// ..., l+448 -- so every fp32 atomic add instruction covers 64 consecutive
+// floats of the dE row.  Atomics are the only cross-wave combination
+// ([LS2] sec. 2.1.2); their order is not fixed.
+constexpr int kChunk = 64;                // tokens per wave (one key per lane)
+constexpr int kSliceCols = kWave * 8;     // columns per wave
+constexpr int kBatch = 16;                // dy rows in flight per lane
 constexpr uint64_t kNoToken = ~0ull;
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
@@ -138,91 +146,93 @@ __device__ __forceinline__ uint64_t wave_sort(uint64_t key, int lane) {
     return key;
 }
 
-// Wave = (chunk of kChunk tokens, all columns); lane l owns column vectors
-// l, l+64, ...  Keys are (id << 8 | local token); invalid ids sort last.
-template <int NV, bool DROP>
-__global__ __launch_bounds__(kBlock) void emb_bwd_chunk_kernel(float* dE, const int32_t* ids,
-                                                               const half_t* dy, uint32_t tokens,
-                                                               uint32_t h, uint32_t vocab,
-                                                               float scale, Dropout d) {
+template <bool DROP>
+__global__ __launch_bounds__(kBlock) void emb_bwd_kernel(float* dE, const int32_t* ids,
+                                                         const half_t* dy, uint32_t tokens,
+                                                         uint32_t h, uint32_t vocab, uint32_t slices,
+                                                         float scale, Dropout d) {
+    __shared__ float xpose[kWaves][kSliceCols];
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t chunk = blockIdx.x * kWaves + threadIdx.x / kWave;
+    const int wave = threadIdx.x / kWave;
+    const uint32_t item = blockIdx.x * kWaves + wave;
+    const uint32_t chunk = item / slices, sl = item - chunk * slices;
     const uint32_t t0 = chunk * kChunk;
     if (t0 >= tokens) return;
     const uint32_t nv = h / 8;
+    const uint32_t cv = sl * kWave + lane;            // this lane's 8-column vector
+    const bool active = cv < nv;
+    float* xp = xpose[wave];
 
+    // Keys (id << 8 | local token); invalid ids and the ragged tail sort last.
     uint64_t key = kNoToken;
-    if (lane < kChunk && t0 + lane < tokens) {
+    if (t0 + lane < tokens) {
         const int32_t id = ids[t0 + lane];
         if (id >= 0 && static_cast<uint32_t>(id) < vocab)
             key = (static_cast<uint64_t>(id) << 8) | static_cast<uint32_t>(lane);
     }
     key = wave_sort(key, lane);
     const uint64_t next = __shfl_down(static_cast<unsigned long long>(key), 1);
-    const bool seg_end = lane == kWave - 1 || (next >> 8) != (key >> 8);
-    const uint64_t ends = __ballot(seg_end);
+    const uint64_t ends = __ballot(lane == kWave - 1 || (next >> 8) != (key >> 8));
     const int count = __popcll(__ballot(key != kNoToken));
 
-    // Fetch the chunk's gradient rows in sorted order, all loads in flight at once.
-    half8 buf[kChunk][NV];
+    float acc[8];
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-        if (j < count) {
-            const uint64_t kj = readlane_u64(key, j);
-            const uint32_t t = t0 + static_cast<uint32_t>(kj & 0xFF);
-            const half8* row = reinterpret_cast<const half8*>(dy + static_cast<size_t>(t) * h);
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    for (int b0 = 0; b0 < count; b0 += kBatch) {
+        half8 g[kBatch];
+        uint32_t tk[kBatch];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const uint32_t cv = lane + v * kWave;
-                if (cv < nv) buf[j][v] = row[cv];
+        for (int j = 0; j < kBatch; ++j) {
+            tk[j] = 0;
+            if (b0 + j < count) {
+                tk[j] = t0 + static_cast<uint32_t>(readlane_u64(key, b0 + j) & 0xFF);
+                if (active) g[j] = reinterpret_cast<const half8*>(dy + static_cast<size_t>(tk[j]) * h)[cv];
             }
         }
-    }
-    float acc[NV][8];
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
+        for (int j = 0; j < kBatch; ++j) {
+            const int pos = b0 + j;
+            if (pos >= count) break;
+            if (active) {
+                float gf[8], f[8];
+                unpack8(g[j], gf);
+                if (DROP) {
+                    dropout_factors8(d, static_cast<uint64_t>(tk[j]) * nv + cv, f);
+                } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[v][k] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-        if (j < count) {
-            const uint64_t kj = readlane_u64(key, j);
-            const uint32_t t = t0 + static_cast<uint32_t>(kj & 0xFF);
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const uint32_t cv = lane + v * kWave;
-                if (cv < nv) {
-                    float g[8], f[8];
-                    unpack8(buf[j][v], g);
-                    if (DROP) {
-                        dropout_factors8(d, static_cast<uint64_t>(t) * nv + cv, f);
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) f[k] = 1.0f;
-                    }
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) acc[v][k] = fmaf(g[k] * f[k], scale, acc[v][k]);
+                    for (int k = 0; k < 8; ++k) f[k] = 1.0f;
                 }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = fmaf(gf[k] * f[k], scale, acc[k]);
             }
-            if ((ends >> j) & 1ull) {
-                float* row = dE + static_cast<size_t>(kj >> 8) * h;
+            if ((ends >> pos) & 1ull) {
+                // Transpose through LDS, then coalesced atomics on the id's row.
+                const uint32_t id = static_cast<uint32_t>(readlane_u64(key, pos) >> 8);
+                float4v* w = reinterpret_cast<float4v*>(xp + lane * 8);
+                w[0] = float4v{acc[0], acc[1], acc[2], acc[3]};
+                w[1] = float4v{acc[4], acc[5], acc[6], acc[7]};
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                float* row = dE + static_cast<size_t>(id) * h + static_cast<size_t>(sl) * kSliceCols;
+                const uint32_t cols = h - sl * kSliceCols;        // columns of this slice present
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const uint32_t cv = lane + v * kWave;
-                    if (cv < nv) {
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            unsafeAtomicAdd(row + cv * 8 + k, acc[v][k]);
-                            acc[v][k] = 0.0f;
-                        }
-                    }
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t c = k * kWave + lane;
+                    if (c < cols) unsafeAtomicAdd(row + c, xp[c]);
                 }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
             }
         }
     }
 }
 
-// Element-wise fallback: one atomic per element.
+// Element-wise fallback (unaligned or hidden % 8 != 0): one fp32 atomic per
+// element, consecutive lanes on consecutive columns.
 template <bool DROP>
 __global__ __launch_bounds__(kBlock) void emb_bwd_scalar_kernel(float* dE, const int32_t* ids,
                                                                 const half_t* dy, uint64_t n,
@@ -379,25 +389,19 @@ int ls_embedding_bwd(float* grad_tok_emb, const int32_t* ids, const void* dy, in
     const uint32_t t32 = static_cast<uint32_t>(tokens), h32 = static_cast<uint32_t>(hidden),
                    v32 = static_cast<uint32_t>(vocab);
     auto* dy16 = static_cast<const half_t*>(dy);
-    const bool vec = hidden % 8 == 0 && hidden <= 1024 && aligned16(dy);
-    if (vec) {
-        const uint32_t chunks = (t32 + kChunk - 1) / kChunk;
-        const unsigned grid = (chunks + kWaves - 1) / kWaves;
-        const int nv = static_cast<int>((hidden / 8 + kWave - 1) / kWave);
-        if (nv == 1) {
-            if (drop) emb_bwd_chunk_kernel<1, true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
-            else emb_bwd_chunk_kernel<1, false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
-        } else {
-            if (drop) emb_bwd_chunk_kernel<2, true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
-            else emb_bwd_chunk_kernel<2, false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, scale, d);
-        }
-        set_dispatch(nv == 1 ? "embedding_bwd/chunk16_nv1" : "embedding_bwd/chunk16_nv2");
+    if (hidden % 8 == 0 && aligned16(dy)) {
+        const uint32_t slices = (h32 + kSliceCols - 1) / kSliceCols;
+        const uint64_t items = static_cast<uint64_t>((t32 + kChunk - 1) / kChunk) * slices;
+        const unsigned grid = static_cast<unsigned>((items + kWaves - 1) / kWaves);
+        if (drop) emb_bwd_kernel<true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
+        else emb_bwd_kernel<false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
+        set_dispatch("embedding_bwd/chunk64_sorted_atomic");
     } else {
         const uint64_t n = static_cast<uint64_t>(tokens) * static_cast<uint64_t>(hidden);
         const unsigned grid = grid_cap((n + kBlock - 1) / kBlock, 65536);
         if (drop) emb_bwd_scalar_kernel<true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, n, h32, v32, scale, d);
         else emb_bwd_scalar_kernel<false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, n, h32, v32, scale, d);
-        set_dispatch("embedding_bwd/scalar");
+        set_dispatch("embedding_bwd/atomic_elementwise");
     }
     return launch_status(name);
 }

@@ -124,77 +124,143 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
 // ---------------------------------------------------------------------------
 // Backward, row pass
 // ---------------------------------------------------------------------------
+// Blocks of 4..16 waves (sized so that ~one block per CU covers the rows);
+// each wave walks its rows with the next row's loads issued before the
+// current row's reductions.  After the rows, the per-lane column
+// accumulators are folded: first across the row groups inside each wave
+// (shuffles), then across waves through one LDS slot per wave, and the block
+// writes its partial row [2h] = (dgamma part, dbeta part).
+template <int CW>
+struct Raw;
+template <>
+struct Raw<8> {
+    using T = half8;
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) {
+        return *reinterpret_cast<const half8*>(p + i);
+    }
+    static __device__ __forceinline__ T zero() { return half8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    static __device__ __forceinline__ void widen(const T& r, float f[8]) { unpack8(r, f); }
+};
+template <>
+struct Raw<1> {
+    using T = half_t;
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ T zero() { return static_cast<half_t>(0.0f); }
+    static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
+};
+
+// Up to 16 waves per block when a lane holds <= 16 elements, else 8 (register
+// budget); the wave slots of the column fold take at most 128 KiB of LDS.
+template <int NCH, int CW>
+struct BwdBounds {
+    static constexpr int kMaxThreads = NCH * CW <= 8 ? 1024 : 512;
+};
+constexpr size_t kBwdLdsBudget = 128 * 1024;
+
 template <int LPR, int NCH, int CW>
-__global__ __launch_bounds__(kBlock) void ln_bwd_kernel(half_t* dx, float* partial,
-                                                        const half_t* dy, const half_t* x,
-                                                        const half_t* gamma, const float* mean,
-                                                        const float* rstd, uint32_t rows,
-                                                        uint32_t h) {
+__global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kernel(half_t* dx, float* partial,
+                                                                const half_t* dy, const half_t* x,
+                                                                const half_t* gamma, const float* mean,
+                                                                const float* rstd, uint32_t rows,
+                                                                uint32_t h) {
+    using R = Raw<CW>;
     constexpr int RPW = kWave / LPR;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
     const int l = lane % LPR;
     const int sub = lane / LPR;
-    extern __shared__ float lds[];     // [2][h]: fixed-order fold of the waves' column sums
+    extern __shared__ float lds[];     // [nwaves][2h]
 
-    float g[NCH][CW], acc_g[NCH][CW], acc_b[NCH][CW];
+    // gamma stays in its fp16 form; rows are widened chunk by chunk, twice
+    // (sums, then dx), so the registers hold raw rows plus the accumulators.
+    typename R::T gr[NCH];
+    float acc_g[NCH][CW], acc_b[NCH][CW];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const uint32_t c = (l + j * LPR) * CW;
-        if (c < h) {
-            Chunk<CW>::load(gamma, c, g[j]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < CW; ++k) g[j][k] = 0.0f;
-        }
+        gr[j] = c < h ? R::load(gamma, c) : R::zero();
 #pragma unroll
         for (int k = 0; k < CW; ++k) acc_g[j][k] = acc_b[j][k] = 0.0f;
     }
     const float inv_h = 1.0f / static_cast<float>(h);
-    for (uint32_t r0 = blockIdx.x * (kWaves * RPW); r0 < rows; r0 += gridDim.x * (kWaves * RPW)) {
-        const uint32_t row = r0 + wave * RPW + sub;
+    const uint32_t per_iter = static_cast<uint32_t>(nwaves) * RPW;
+    const uint32_t stride = gridDim.x * per_iter;
+    const uint32_t my = static_cast<uint32_t>(wave) * RPW + sub;
+
+    // Loads of one row: raw fp16 chunks and the saved statistics.
+    typename R::T rdy[NCH], rx[NCH];
+    float mu = 0.0f, rs = 0.0f;
+    auto fetch = [&](uint32_t row, typename R::T* ody, typename R::T* ox, float& omu, float& ors) {
         const bool ok = row < rows;
         const size_t base = static_cast<size_t>(row) * h;
-        float vdy[NCH][CW], vx[NCH][CW];
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
             if (ok && c < h) {
-                Chunk<CW>::load(dy, base + c, vdy[j]);
-                Chunk<CW>::load(x, base + c, vx[j]);
+                ody[j] = R::load(dy, base + c);
+                ox[j] = R::load(x, base + c);
             } else {
-#pragma unroll
-                for (int k = 0; k < CW; ++k) vdy[j][k] = vx[j][k] = 0.0f;
+                ody[j] = R::zero();
+                ox[j] = R::zero();
             }
         }
-        const float mu = ok ? mean[row] : 0.0f;
-        const float rs = ok ? rstd[row] : 0.0f;
+        omu = ok ? mean[row] : 0.0f;
+        ors = ok ? rstd[row] : 0.0f;
+    };
+    uint32_t r0 = blockIdx.x * per_iter;
+    if (r0 < rows) fetch(r0 + my, rdy, rx, mu, rs);
+    for (; r0 < rows; r0 += stride) {
+        const uint32_t row = r0 + my;
+        typename R::T ndy[NCH], nx[NCH];
+        float nmu = 0.0f, nrs = 0.0f;
+        if (r0 + stride < rows) fetch(row + stride, ndy, nx, nmu, nrs);   // prefetch the next row
+
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j)
+        for (int j = 0; j < NCH; ++j) {
+            float fd[CW], fx[CW], fg[CW];
+            R::widen(rdy[j], fd);
+            R::widen(rx[j], fx);
+            R::widen(gr[j], fg);
 #pragma unroll
             for (int k = 0; k < CW; ++k) {
-                const float xh = (vx[j][k] - mu) * rs;
-                const float gd = g[j][k] * vdy[j][k];
-                vx[j][k] = xh;                         // keep xhat
+                const float xh = (fx[k] - mu) * rs;
+                const float gd = fg[k] * fd[k];
                 sa += gd;
                 sb = fmaf(gd, xh, sb);
-                acc_g[j][k] = fmaf(vdy[j][k], xh, acc_g[j][k]);
-                acc_b[j][k] += vdy[j][k];
+                acc_g[j][k] = fmaf(fd[k], xh, acc_g[j][k]);
+                acc_b[j][k] += fd[k];
             }
+        }
         sa = group_sum<LPR>(sa);          // the two row sums, reduced together
         sb = group_sum<LPR>(sb);
         const float ca = sa * inv_h, cb = sb * inv_h;
+        if (row < rows) {
+            const size_t base = static_cast<size_t>(row) * h;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (ok && c < h) {
-                float o[CW];
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                if (c < h) {
+                    float fd[CW], fx[CW], fg[CW], o[CW];
+                    R::widen(rdy[j], fd);
+                    R::widen(rx[j], fx);
+                    R::widen(gr[j], fg);
 #pragma unroll
-                for (int k = 0; k < CW; ++k)
-                    o[k] = rs * (g[j][k] * vdy[j][k] - fmaf(vx[j][k], cb, ca));
-                Chunk<CW>::store(dx, base + c, o);
+                    for (int k = 0; k < CW; ++k)
+                        o[k] = rs * (fg[k] * fd[k] - fmaf((fx[k] - mu) * rs, cb, ca));
+                    Chunk<CW>::store(dx, base + c, o);
+                }
             }
+        }
+        if (r0 + stride < rows) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                rdy[j] = ndy[j];
+                rx[j] = nx[j];
+            }
+            mu = nmu;
+            rs = nrs;
         }
     }
 
@@ -208,58 +274,72 @@ __global__ __launch_bounds__(kBlock) void ln_bwd_kernel(half_t* dx, float* parti
                 acc_g[j][k] += __shfl_xor(acc_g[j][k], o);
                 acc_b[j][k] += __shfl_xor(acc_b[j][k], o);
             }
-    // Fold the waves in order 0, 1, 2, 3 through LDS.
-    for (int w = 0; w < kWaves; ++w) {
-        if (wave == w && sub == 0) {
+    // Every wave parks its column sums in its own LDS slot [wave][2h]; after
+    // one barrier each thread sums whole columns over the slots in wave order
+    // and writes the block's partial row.  The order is fixed, so the sums are.
+    if (sub == 0) {
+        float* mine = lds + static_cast<size_t>(wave) * 2 * h;
 #pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const uint32_t c = (l + j * LPR) * CW;
-                if (c < h) {
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            if (c < h) {
+                if constexpr (CW == 8) {      // two 16-byte LDS stores per half
+                    float4v* pg = reinterpret_cast<float4v*>(mine + c);
+                    float4v* pb = reinterpret_cast<float4v*>(mine + h + c);
+                    pg[0] = float4v{acc_g[j][0], acc_g[j][1], acc_g[j][2], acc_g[j][3]};
+                    pg[1] = float4v{acc_g[j][4], acc_g[j][5], acc_g[j][6], acc_g[j][7]};
+                    pb[0] = float4v{acc_b[j][0], acc_b[j][1], acc_b[j][2], acc_b[j][3]};
+                    pb[1] = float4v{acc_b[j][4], acc_b[j][5], acc_b[j][6], acc_b[j][7]};
+                } else {
 #pragma unroll
                     for (int k = 0; k < CW; ++k) {
-                        lds[c + k] = (w == 0 ? 0.0f : lds[c + k]) + acc_g[j][k];
-                        lds[h + c + k] = (w == 0 ? 0.0f : lds[h + c + k]) + acc_b[j][k];
+                        mine[c + k] = acc_g[j][k];
+                        mine[h + c + k] = acc_b[j][k];
                     }
                 }
             }
         }
-        __syncthreads();
     }
+    __syncthreads();
     float* out = partial + static_cast<size_t>(blockIdx.x) * 2 * h;
-    for (uint32_t c = threadIdx.x; c < 2 * h; c += kBlock) out[c] = lds[c];
+    for (uint32_t col = threadIdx.x; col < 2 * h; col += blockDim.x) {
+        float t = 0.0f;
+        for (int w = 0; w < nwaves; ++w) t += lds[static_cast<size_t>(w) * 2 * h + col];
+        out[col] = t;
+    }
 }
 
-// Column finalisation: dgamma[c] = sum_b partial[b][0][c], dbeta likewise.
-// 16 slices of blocks are summed by 16 thread rows, then the slices in order.
+// Column finalisation over the [nblocks][2h] partials: column c of the 2h
+// (dgamma then dbeta) is summed by 16 thread slices (slice s takes blocks
+// s, s+16, ...), then the 16 slice sums in order.  nblocks <= 256, so every
+// thread issues at most 16 independent loads.
+constexpr int kFinCols = 16;
 constexpr int kFinSlices = 16;
-__global__ __launch_bounds__(kFinSlices * 64) void ln_bwd_finalize_kernel(half_t* dgamma,
-                                                                          half_t* dbeta,
-                                                                          const float* partial,
-                                                                          uint32_t nblocks,
-                                                                          uint32_t h) {
-    __shared__ float sg[kFinSlices][64], sb[kFinSlices][64];
-    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
-    const uint32_t c = blockIdx.x * 64 + cl;
-    float ag = 0.0f, ab = 0.0f;
-    if (c < h) {
-        for (uint32_t bidx = k; bidx < nblocks; bidx += kFinSlices) {
-            const float* p = partial + static_cast<size_t>(bidx) * 2 * h;
-            ag += p[c];
-            ab += p[h + c];
-        }
-    }
-    sg[k][cl] = ag;
-    sb[k][cl] = ab;
-    __syncthreads();
-    if (k == 0 && c < h) {
-        float tg = 0.0f, tb = 0.0f;
+constexpr unsigned kMaxBwdBlocks = kFinSlices * 16;
+
+__global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
+    half_t* dgamma, half_t* dbeta, const float* partial, uint32_t nblocks, uint32_t h) {
+    __shared__ float sums[kFinSlices][kFinCols];
+    const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
+    const uint32_t c = blockIdx.x * kFinCols + cl;
+    const uint32_t w = 2 * h;
+    float v[16];
 #pragma unroll
-        for (int s = 0; s < kFinSlices; ++s) {
-            tg += sg[s][cl];
-            tb += sb[s][cl];
-        }
-        dgamma[c] = static_cast<half_t>(tg);
-        dbeta[c] = static_cast<half_t>(tb);
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t b = sl + i * kFinSlices;
+        v[i] = (c < w && b < nblocks) ? partial[static_cast<size_t>(b) * w + c] : 0.0f;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a += v[i];
+    sums[sl][cl] = a;
+    __syncthreads();
+    if (sl == 0 && c < w) {
+        float t = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kFinSlices; ++s) t += sums[s][cl];
+        if (c < h) dgamma[c] = static_cast<half_t>(t);
+        else dbeta[c - h] = static_cast<half_t>(t);
     }
 }
 
@@ -278,8 +358,7 @@ bool ln_shape(int64_t h, bool vec, LnShape* s) {
         else if (nv <= 16) *s = {16, 1, 8, "lpr16_nch1_v8"};
         else if (nv <= 32) *s = {16, 2, 8, "lpr16_nch2_v8"};
         else if (nv <= 64) *s = {32, 2, 8, "lpr32_nch2_v8"};
-        else if (nv <= 96) *s = {32, 3, 8, "lpr32_nch3_v8"};
-        else if (nv <= 128) *s = {32, 4, 8, "lpr32_nch4_v8"};
+        else if (nv <= 128) *s = {64, 2, 8, "lpr64_nch2_v8"};
         else if (nv <= 256) *s = {64, 4, 8, "lpr64_nch4_v8"};
         else if (nv <= 512) *s = {64, 8, 8, "lpr64_nch8_v8"};
         else return false;
@@ -297,7 +376,7 @@ bool ln_shape(int64_t h, bool vec, LnShape* s) {
 }
 
 constexpr int64_t kMaxHidden = 4096;
-constexpr unsigned kMaxBwdBlocks = 256;
+constexpr int kNumCU = 256;
 
 unsigned fwd_grid(int64_t rows, const LnShape& s) {
     const int64_t per_block = kWaves * (kWave / s.lpr);
@@ -305,27 +384,51 @@ unsigned fwd_grid(int64_t rows, const LnShape& s) {
     return static_cast<unsigned>(g < (1 << 20) ? g : (1 << 20));
 }
 
-unsigned bwd_grid(int64_t rows, int64_t h) {
-    LnShape s;
-    if (!ln_shape(h, h % 8 == 0, &s)) ln_shape(h, false, &s);
-    const int64_t per_block = kWaves * (kWave / s.lpr);
+// Backward launch: waves per block (a power of two, 4 up to the shape's
+// register and LDS limits) so that about one block per CU covers every row,
+// then the block count (at most 256).
+struct BwdLaunch {
+    int waves;
+    unsigned grid;
+    size_t lds_bytes;
+};
+
+BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
+    BwdLaunch b;
+    const int64_t rpw = kWave / s.lpr;
+    const int max_waves = (s.nch * s.cw <= 8 ? 1024 : 512) / kWave;
+    const int64_t want = (rows + kNumCU * rpw - 1) / (kNumCU * rpw);   // waves per block for one pass
+    b.waves = 4;
+    while (b.waves < max_waves && b.waves < want &&
+           static_cast<size_t>(2 * b.waves) * 2 * h * sizeof(float) <= kBwdLdsBudget)
+        b.waves *= 2;
+    const int64_t per_block = b.waves * rpw;
     const int64_t g = (rows + per_block - 1) / per_block;
-    return static_cast<unsigned>(g < kMaxBwdBlocks ? g : kMaxBwdBlocks);
+    b.grid = static_cast<unsigned>(g < kMaxBwdBlocks ? g : kMaxBwdBlocks);
+    b.lds_bytes = static_cast<size_t>(b.waves) * 2 * h * sizeof(float);
+    return b;
 }
 
 #define LS_LN_FWD(LPR, NCH, CW)                                                                 \
     ln_fwd_kernel<LPR, NCH, CW><<<grid, kBlock, 0, st>>>(y16, mean, rstd, x16, g16, b16, r32, h32, eps)
 #define LS_LN_BWD(LPR, NCH, CW)                                                                 \
-    ln_bwd_kernel<LPR, NCH, CW><<<grid, kBlock, lds_bytes, st>>>(dx16, part, dy16, x16, g16, mean, rstd, r32, h32)
+    do {                                                                                        \
+        if (bl.lds_bytes > 65536 &&                                                             \
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&ln_bwd_kernel<LPR, NCH, CW>),   \
+                                hipFuncAttributeMaxDynamicSharedMemorySize,                    \
+                                static_cast<int>(bl.lds_bytes)) != hipSuccess)                  \
+            return fail(LS_ERR_HIP, "%s: cannot reserve %zu bytes of LDS", name, bl.lds_bytes); \
+        ln_bwd_kernel<LPR, NCH, CW><<<bl.grid, bl.waves * kWave, bl.lds_bytes, st>>>(          \
+            dx16, part, dy16, x16, g16, mean, rstd, r32, h32);                                  \
+    } while (0)
 
 #define LS_LN_TABLE(M)                                                                          \
     if (s.cw == 8) {                                                                            \
         if (s.lpr == 8) M(8, 1, 8);                                                             \
         else if (s.lpr == 16 && s.nch == 1) M(16, 1, 8);                                        \
         else if (s.lpr == 16) M(16, 2, 8);                                                      \
-        else if (s.lpr == 32 && s.nch == 2) M(32, 2, 8);                                        \
-        else if (s.lpr == 32 && s.nch == 3) M(32, 3, 8);                                        \
-        else if (s.lpr == 32) M(32, 4, 8);                                                      \
+        else if (s.lpr == 32) M(32, 2, 8);                                                      \
+        else if (s.nch == 2) M(64, 2, 8);                                                       \
         else if (s.nch == 4) M(64, 4, 8);                                                       \
         else M(64, 8, 8);                                                                       \
     } else {                                                                                    \
@@ -380,7 +483,9 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
 
 size_t ls_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
     if (rows <= 0 || hidden <= 0 || hidden > ls::kMaxHidden) return 0;
-    return static_cast<size_t>(ls::bwd_grid(rows, hidden)) * 2 * static_cast<size_t>(hidden) * sizeof(float);
+    // Upper bound of the partial rows over every launch shape of (rows, hidden).
+    const int64_t blocks = rows < ls::kMaxBwdBlocks ? rows : ls::kMaxBwdBlocks;
+    return static_cast<size_t>(blocks) * 2 * static_cast<size_t>(hidden) * sizeof(float);
 }
 
 int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
@@ -406,8 +511,7 @@ int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const 
     const bool vec = hidden % 8 == 0 && aligned16(dx) && aligned16(dy) && aligned16(x) && aligned16(gamma);
     LnShape s;
     ln_shape(hidden, vec, &s);
-    const unsigned grid = bwd_grid(rows, hidden);
-    const size_t lds_bytes = 2 * static_cast<size_t>(hidden) * sizeof(float);
+    const BwdLaunch bl = bwd_launch(rows, hidden, s);
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto* dx16 = static_cast<half_t*>(dx);
     auto* dy16 = static_cast<const half_t*>(dy);
@@ -419,12 +523,12 @@ int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const 
     LS_LN_TABLE(LS_LN_BWD)
     int rc = launch_status(name);
     if (rc != LS_OK) return rc;
-    const unsigned fgrid = static_cast<unsigned>((hidden + 63) / 64);
-    ln_bwd_finalize_kernel<<<fgrid, kFinSlices * 64, 0, st>>>(static_cast<half_t*>(dgamma),
-                                                               static_cast<half_t*>(dbeta), part,
-                                                               grid, h32);
+    const unsigned fgrid = static_cast<unsigned>((2 * hidden + kFinCols - 1) / kFinCols);
+    ln_bwd_finalize_kernel<<<fgrid, kFinCols * kFinSlices, 0, st>>>(static_cast<half_t*>(dgamma),
+                                                                     static_cast<half_t*>(dbeta), part,
+                                                                     bl.grid, h32);
     char buf[96];
-    snprintf(buf, sizeof(buf), "layernorm_bwd/%s_g%u", s.name, grid);
+    snprintf(buf, sizeof(buf), "layernorm_bwd/%s_w%d_g%u", s.name, bl.waves, bl.grid);
     set_dispatch(buf);
     return launch_status(name);
 }

@@ -105,6 +105,7 @@ def test_embedding_validation(lib):
     assert lib.ls_embedding_fwd(FAKE, None, FAKE, FAKE, 2, 16, 8, 10, 16, 1.0, 0.1, 1, 0, s) == LS_ERR_NULL
     assert lib.ls_embedding_bwd(None, FAKE, FAKE, 2, 16, 8, 10, 1.0, 0.1, 1, 0, 1, s) == LS_ERR_NULL
     assert lib.ls_embedding_bwd(FAKE, FAKE, FAKE, -2, 16, 8, 10, 1.0, 0.1, 1, 0, 1, s) == LS_ERR_SHAPE
+    assert lib.ls_embedding_bwd(FAKE, FAKE, FAKE, 2, 16, 8, 10, 1.0, 1.1, 1, 0, 1, s) == LS_ERR_PARAM
     assert lib.ls_embedding_bwd(None, None, None, 0, 16, 8, 0, 1.0, 0.1, 1, 0, 1, s) == LS_OK
 
 

@@ -313,6 +313,52 @@ def test_embedding_c4(ls):
     assert np.all(err <= 1e-5 * mag + 1e-30), f"embedding_bwd [{last_dispatch()}]: max err {err.max()}"
     untouched = np.setdiff1d(np.arange(v), ids)
     assert np.all(got[untouched] == 0)
+    assert "chunk64" in last_dispatch()
+
+
+def _emb_bwd_check(ls, ids, dy, v, s, p, seed, off, acc=None, what=""):
+    h = dy.shape[-1]
+    dE = dev(acc.copy()) if acc is not None else torch.zeros((v, h), dtype=torch.float32, device="cuda")
+    ls.embedding_bwd(dev(ids), dev(dy), dE, s, p, seed, off, zero_first=acc is None)
+    got = host(dE).astype(np.float64)
+    want = oracle.embedding_bwd(ids, dy, v, s, p, seed, off, BITS, grad_in=acc).astype(np.float64)
+    keep = oracle.dropout_keep(ids.size * h, p, seed, off, BITS).reshape(-1, h)
+    terms = np.abs(s * dy.astype(np.float64).reshape(-1, h) * keep * oracle.dropout_scale(p, BITS))
+    mag = np.zeros((v, h)) if acc is None else np.abs(acc.astype(np.float64))
+    ok_ids = (ids.reshape(-1) >= 0) & (ids.reshape(-1) < v)
+    np.add.at(mag, ids.reshape(-1)[ok_ids], terms[ok_ids])
+    err = np.abs(got - want)
+    assert np.all(err <= 1e-5 * mag + 1e-30), f"{what} [{last_dispatch()}]: max err {err.max()}"
+    return last_dispatch()
+
+
+@pytest.mark.parametrize("counts,h", [([1], 768), ([64], 768), ([65], 1024), ([2000], 768),
+                                      ([31, 33, 97, 1], 520), ([7] * 40, 1536)])
+def test_embedding_bwd_repeated_ids(ls, counts, h):
+    """Runs of one id inside and across 64-token chunks, column slices with
+    a ragged last slice (520, 1536 columns)."""
+    g = np.random.default_rng(sum(counts) + h)
+    ids = np.concatenate([np.full(c, 5 + 3 * i, np.int32) for i, c in enumerate(counts)])
+    ids = g.permutation(ids)
+    pad = (-ids.size) % 4
+    ids = np.concatenate([ids, np.full(pad, 2, np.int32)]).reshape(4, -1)
+    dy = synth.normal16(g, (ids.size, h), 1.0)
+    disp = _emb_bwd_check(ls, ids, dy, 300, 32.0, 0.1, 21, 3, what=f"counts {counts} h={h}")
+    assert "chunk64" in disp
+
+
+def test_embedding_bwd_other_paths(ls):
+    g = np.random.default_rng(4)
+    ids = g.integers(0, 50, size=(40, 500)).astype(np.int32)          # 20000 tokens
+    dy = synth.normal16(g, (ids.size, 64), 1.0)
+    _emb_bwd_check(ls, ids, dy, 50, 2.0, 0.1, 9, 3, what="20000 tokens")
+    ids = g.integers(0, 9, size=(3, 11)).astype(np.int32)             # hidden not a multiple of 8
+    dy = synth.normal16(g, (ids.size, 20), 1.0)
+    assert "elementwise" in _emb_bwd_check(ls, ids, dy, 9, 2.0, 0.0, 9, 3, what="hidden 20")
+    ids = g.integers(0, 1 << 20, size=(2, 300)).astype(np.int32)      # wide vocabulary, sparse hits
+    ids[0, :50] = (1 << 20) - 1
+    dy = synth.normal16(g, (ids.size, 64), 1.0)
+    _emb_bwd_check(ls, ids, dy, 1 << 20, 2.0, 0.1, 9, 3, what="vocab 2^20")
 
 
 @pytest.mark.parametrize("b,l,h,v", [(2, 7, 64, 50), (3, 5, 768, 100), (1, 33, 24, 9), (2, 4, 20, 11),
