@@ -10,11 +10,12 @@ arithmetic, dropout 0.1):
 
 Inputs are synthetic (seeded, shaped like the layer) and resident in HBM before
 the timed region.  R independent buffer sets (> 2 GB in total) are rotated so
-that no step finds its tensors in the 256 MB Infinity Cache.  Each set's chain is
-captured in HIP graphs, except the largest kernel (bias+ReLU+dropout), which is
-launched directly between two HIP events on the same stream (created without
-the system-scope fence, so they bracket the kernel alone): the events give that
-kernel's average duration live inside the timed region (the roofline line).
+that no step finds its tensors in the 256 MB Infinity Cache.  Each set's step is
+captured as one HIP graph.  Every 8th timed step is replayed split around the
+largest kernel (bias+ReLU+dropout), which is then launched directly between two
+HIP events on the same stream (created without the system-scope fence, so they
+bracket the kernel alone): the events sample that kernel's duration live inside
+the timed region (the roofline line).
 
 Output: one JSON line.  `value` is algorithmic chain bytes per second (the
 fused-minimum bytes: every input read once, every output written once, the
@@ -441,52 +442,59 @@ def main():
         s.run(check)
     torch.cuda.synchronize()
 
-    # Per set: graph A (launches before the dominant kernel), the dominant
-    # kernel direct, graph B (launches after it).
+    # Per set: one graph of the whole step, and the same step split around the
+    # dominant kernel (graph A, the kernel launched directly between two
+    # fence-free events, graph B).  Every SAMPLE-th step of the timed region
+    # is a split one, so the events sample the kernel live while the other
+    # steps run as single graphs.
     dom_idx = [i for i, l in enumerate(sets[0].launches) if l[0] == DOMINANT][0]
-    graphs = []
     cap_stream = torch.cuda.Stream()
-    for s in sets:
-        ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(ga, stream=cap_stream):
+
+    def capture(s, lo, hi):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
             st = torch.cuda.current_stream().cuda_stream
-            for name, _, fn, a in s.launches[:dom_idx]:
+            for name, _, fn, a in s.launches[lo:hi]:
                 check(name, fn(*a[:-1], st))
-        with torch.cuda.graph(gb, stream=cap_stream):
-            st = torch.cuda.current_stream().cuda_stream
-            for name, _, fn, a in s.launches[dom_idx + 1:]:
-                check(name, fn(*a[:-1], st))
-        graphs.append((ga, gb))
+        return g
+    n_launch = len(sets[0].launches)
+    graphs = [(capture(s, 0, n_launch), capture(s, 0, dom_idx), capture(s, dom_idx + 1, n_launch)) for s in sets]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     S = stream.cuda_stream
     dom = [(s.launches[dom_idx][2], s.launches[dom_idx][3][:-1] + (S,)) for s in sets]
+    SAMPLE = 8
 
     def step(i, ev=None):
+        s = sets[i % len(sets)]
+        g_full, g_a, g_b = graphs[i % len(graphs)]
+        sampled = ev is not None and i % SAMPLE == 0
+        if not args.eager and not sampled:
+            g_full.replay()
+            return
         fn, a = dom[i % len(dom)]
         if args.eager:
-            s = sets[i % len(sets)]
             for nm, _, f, aa in s.launches[:dom_idx]:
                 f(*aa)
         else:
-            graphs[i % len(graphs)][0].replay()
-        if ev is not None:
-            ev.record(i, 0, S)
+            g_a.replay()
+        if sampled:
+            ev.record(i // SAMPLE, 0, S)
         fn(*a)
-        if ev is not None:
-            ev.record(i, 1, S)
+        if sampled:
+            ev.record(i // SAMPLE, 1, S)
         if args.eager:
             for nm, _, f, aa in s.launches[dom_idx + 1:]:
                 f(*aa)
         else:
-            graphs[i % len(graphs)][1].replay()
+            g_b.replay()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    kev = KernelEvents(K)
+    kev = KernelEvents((K + SAMPLE - 1) // SAMPLE)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()

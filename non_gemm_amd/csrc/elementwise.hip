@@ -26,8 +26,10 @@ __global__ __launch_bounds__(kBlock) void elementwise_vec_kernel(
     for (int j = 0; j < VPT; ++j) {
         const uint32_t v = base + j * kBlock;
         if (v < nvec) {
-            xv[j] = x[v];
-            if (RESID) rv[j] = res[v];
+            // Streamed operands: non-temporal loads and stores keep them from
+            // displacing reusable lines (the bias) in the caches.
+            xv[j] = __builtin_nontemporal_load(x + v);
+            if (RESID) rv[j] = __builtin_nontemporal_load(res + v);
             bv[j] = bias[col_vecs.mod(v)];
         }
     }
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(kBlock) void elementwise_vec_kernel(
                 if (RELU) t = t < 0.0f ? 0.0f : t;   // NaN propagates
                 o[k] = RESID ? fmaf(f[k], t, r[k]) : t * f[k];
             }
-            out[v] = pack8(o);
+            __builtin_nontemporal_store(pack8(o), out + v);
         }
     }
 }

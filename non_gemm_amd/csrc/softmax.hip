@@ -27,13 +27,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int CW>
 struct Chunk;
+// Score rows are streamed once: non-temporal 16-byte loads and stores.
 template <>
 struct Chunk<8> {
     static __device__ __forceinline__ void load(const half_t* p, size_t i, float f[8]) {
-        unpack8(*reinterpret_cast<const half8*>(p + i), f);
+        unpack8(__builtin_nontemporal_load(reinterpret_cast<const half8*>(p + i)), f);
     }
     static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[8]) {
-        *reinterpret_cast<half8*>(p + i) = pack8(f);
+        __builtin_nontemporal_store(pack8(f), reinterpret_cast<half8*>(p + i));
     }
 };
 template <>
