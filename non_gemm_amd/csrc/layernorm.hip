@@ -34,8 +34,10 @@ struct Chunk<8> {
     static __device__ __forceinline__ void load(const half_t* p, size_t i, float f[8]) {
         unpack8(*reinterpret_cast<const half8*>(p + i), f);
     }
+    // Outputs (y, dx) are written once and not read again by this kernel:
+    // non-temporal stores keep them from displacing the reused gamma / beta.
     static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[8]) {
-        *reinterpret_cast<half8*>(p + i) = pack8(f);
+        __builtin_nontemporal_store(pack8(f), reinterpret_cast<half8*>(p + i));
     }
 };
 
