@@ -375,6 +375,46 @@ def stored_traffic():
 
 # ---------------------------------------------------------------------------
 
+def attainable(torch, lib, check, cap_stream, dom_bytes):
+    """Bandwidth the device reaches with the operators' access pattern: the
+    library's reference copy and read kernels over 1 GiB buffers, and a copy
+    moving the dominant kernel's byte count, rotated over enough buffers to
+    stay out of the 256 MB Infinity Cache."""
+    def rate(pairs, fn, moved, reps=10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            st = torch.cuda.current_stream().cuda_stream
+            for a, b in pairs:
+                check(fn.__name__, fn(a.data_ptr(), b.data_ptr(), b.numel(), st))
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(pairs))
+        return round(moved / us / 1e3, 1), round(us, 2)
+
+    out = {"kernels": "ls_probe_copy / ls_probe_read (16-byte non-temporal accesses, 256-thread blocks)"}
+    big = 1 << 30
+    pairs = [(torch.empty(big, dtype=torch.uint8, device="cuda"), torch.ones(big, dtype=torch.uint8, device="cuda"))
+             for _ in range(2)]
+    out["copy_1GiB_GBps"], _ = rate(pairs, lib.ls_probe_copy, 2 * big)
+    sinks = [(torch.empty(big // 1024, dtype=torch.float32, device="cuda"), b) for _, b in pairs]
+    out["read_1GiB_GBps"], _ = rate(sinks, lib.ls_probe_read, big + big // 256)
+    del pairs, sinks
+    half = (dom_bytes // 2) // 16 * 16
+    pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda"), torch.ones(half, dtype=torch.uint8, device="cuda"))
+             for _ in range(24)]
+    out["copy_dominant_bytes_GBps"], out["copy_dominant_bytes_us"] = rate(pairs, lib.ls_probe_copy, 2 * half)
+    out["copy_dominant_bytes"] = 2 * half
+    del pairs
+    torch.cuda.empty_cache()
+    return out
+
+
 def warm_chain_us(torch, s, cap_stream, check, reps=100):
     """One buffer set replayed back to back: the chain with its tensors cache-resident."""
     g = torch.cuda.CUDAGraph()
@@ -410,8 +450,8 @@ def main():
         summarize_counters(*args.summarize_counters)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU leg in this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the operators "
+              "shard by token rows with no exchange, and that multi-GPU leg is not built", file=sys.stderr)
         return 2
 
     import torch
@@ -544,6 +584,7 @@ def main():
     torch.cuda.synchronize()
     del graphs, sets
     torch.cuda.empty_cache()
+    reach = None if args.no_info else attainable(torch, lib, check, cap_stream, per[DOMINANT])
 
     extra = None if args.no_extra else extra_rows(torch, ops)
     cpu = None if args.no_cpu else cpu_baseline(shape, p, seed, eps)
@@ -576,6 +617,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_cold": kernels,
         "warm_chain_us": None if warm_us is None else round(warm_us, 2),
+        "attainable_hbm": reach,
         "dispatch": dispatch,
         "other_rows": extra,
         "wall_s_timed": round(wall, 4),

@@ -189,6 +189,27 @@ int ls_adam_workspace_step(void* param, const void* grad, float* exp_avg, float*
 int ls_dropout_mask(uint8_t* keep, int64_t n, float p, uint64_t seed, uint64_t offset,
                     void* stream);
 
+/* ---------------------------------------------------------------------
+ * Bandwidth reference kernels (measurement)
+ * ---------------------------------------------------------------------
+ * The roofline that bounds every operator above is HBM bandwidth ([CS336]
+ * sec. 2.2).  These two kernels give the bandwidth this device actually
+ * reaches with the operators' access pattern (one 16-byte non-temporal
+ * access per lane, one 256-thread block per 4 KiB), so that a kernel's
+ * achieved GB/s can be read against it as well as against the data-sheet
+ * peak.  They compute nothing the operators need.
+ *
+ * ls_probe_copy: dst[0, bytes) = src[0, bytes).  bytes is a multiple of 16,
+ *   both pointers are 16-byte aligned device pointers, no overlap.
+ * ls_probe_read: reads src[0, bytes) as fp32 and writes, for every 1 KiB of
+ *   it, the sum of that KiB's 256 floats to sink (ceil(bytes / 1024) floats,
+ *   16-byte aligned): 0.4 % extra traffic that keeps every load live.
+ * Errors: LS_ERR_SHAPE for a negative or non-multiple-of-16 size,
+ *   LS_ERR_NULL for a null pointer with bytes > 0, LS_ERR_PARAM for a
+ *   pointer that is not 16-byte aligned.  bytes == 0 is a no-op. */
+int ls_probe_copy(void* dst, const void* src, int64_t bytes, void* stream);
+int ls_probe_read(float* sink, const void* src, int64_t bytes, void* stream);
+
 /* Width in bits of the random field behind one dropout decision (16). */
 int ls_dropout_decision_bits(void);
 

@@ -41,6 +41,8 @@ SIGNATURES = {
     "ls_adam_workspace_step": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_f32,
                                        c_f32, c_f32, c_f32, c_f32, c_i64, c_f32, c_int, c_void_p]),
     "ls_dropout_mask": (c_int, [c_void_p, c_i64, c_f32, c_u64, c_u64, c_void_p]),
+    "ls_probe_copy": (c_int, [c_void_p, c_void_p, c_i64, c_void_p]),
+    "ls_probe_read": (c_int, [c_void_p, c_void_p, c_i64, c_void_p]),
     "ls_dropout_decision_bits": (c_int, []),
     "ls_status_string": (ctypes.c_char_p, [c_int]),
     "ls_last_error": (ctypes.c_char_p, []),

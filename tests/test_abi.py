@@ -119,3 +119,15 @@ def test_adam_validation(lib):
     assert lib.ls_adam_workspace_step(*a, -1.0, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 1, s) == LS_ERR_PARAM
     assert lib.ls_adam_workspace_step(FAKE, None, FAKE, FAKE, 100, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 1, s) == LS_ERR_NULL
     assert lib.ls_adam_workspace_step(None, None, None, None, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 1, s) == LS_OK
+
+
+def test_probe_validation(lib):
+    s = None
+    assert lib.ls_probe_copy(FAKE, FAKE, 24, s) == LS_ERR_SHAPE
+    assert lib.ls_probe_copy(FAKE, FAKE, -16, s) == LS_ERR_SHAPE
+    assert lib.ls_probe_copy(None, FAKE, 32, s) == LS_ERR_NULL
+    assert lib.ls_probe_copy(ctypes.c_void_p(0x1008), FAKE, 32, s) == LS_ERR_PARAM
+    assert lib.ls_probe_copy(None, None, 0, s) == LS_OK
+    assert lib.ls_probe_read(None, FAKE, 1024, s) == LS_ERR_NULL
+    assert lib.ls_probe_read(FAKE, FAKE, 1000, s) == LS_ERR_SHAPE
+    assert lib.ls_probe_read(None, None, 0, s) == LS_OK

@@ -462,3 +462,30 @@ def test_adam_resume_bit_identical(ls):
     assert torch.equal(ws1.exp_avg, ws3.exp_avg) and torch.equal(ws1.exp_avg_sq, ws3.exp_avg_sq)
     # parameters are views of the workspace
     assert torch.equal(ps3[2].detach().reshape(-1), ws3.param[ws3.offsets[2]:ws3.offsets[2] + 3072 * 768])
+
+
+# ----------------------------------------------------------------------------
+# Bandwidth reference kernels (measurement only): exact copy, per-KiB sums
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 4096 * 5 + 48, 1 << 24])
+def test_probe_copy_and_read(ls, nbytes):
+    from non_gemm_amd import _lib
+    lib = _lib.load()
+    S = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(nbytes)
+    src_np = rng.standard_normal(nbytes // 4).astype(np.float32)
+    src = dev(src_np)
+    dst = torch.full_like(src, float("nan"))
+    _lib.check("ls_probe_copy", lib.ls_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, S))
+    assert np.array_equal(host(dst).view(np.uint32), src_np.view(np.uint32))
+    nsink = -(-nbytes // 1024)
+    sink = torch.full((nsink + 4,), -7.0, dtype=torch.float32, device="cuda")
+    _lib.check("ls_probe_read", lib.ls_probe_read(sink.data_ptr(), src.data_ptr(), nbytes, S))
+    got = host(sink)
+    pad = np.zeros(nsink * 256, np.float64)
+    pad[:src_np.size] = src_np
+    want = pad.reshape(nsink, 256).sum(axis=1)
+    scale = np.abs(pad).reshape(nsink, 256).sum(axis=1)
+    assert np.all(np.abs(got[:nsink] - want) <= 1e-5 * scale + 1e-30)
+    assert np.all(got[nsink:] == -7.0)        # nothing written past ceil(bytes / 1024)
