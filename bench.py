@@ -252,49 +252,96 @@ def cpu_baseline(shape, p, seed, eps, min_seconds=10.0, max_seconds=30.0):
 # shape, Adam over the 350M-parameter workspace)
 # ---------------------------------------------------------------------------
 
-def extra_rows(torch, ops, iters=20):
+def extra_rows(torch, ops):
+    """The rows outside the C3 chain, each on rotated buffer sets (cold): the
+    elementwise backward pair at the C3 shapes, the C4 embedding forward and
+    backward, and Adam over the 350M-parameter workspace."""
     import numpy as np
 
     import synth
     out = {}
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    inp = synth.embedding_inputs()
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
-    ids, E, P, dy = d(inp["ids"]), d(inp["tok_emb"]), d(inp["pos_emb"]), d(inp["grad_out"])
-    T, H = dy.shape
-    V = E.shape[0]
-    emb_out = torch.empty((T, H), dtype=torch.float16, device="cuda")
-    dE = torch.zeros((V, H), dtype=torch.float32, device="cuda")
-    distinct = int(np.unique(inp["ids"]).size)
     seed, p = synth.DROPOUT_SEED, synth.DROPOUT_P
-    for _ in range(3):
-        ops.embedding_fwd(ids, E, P, inp["scale"], p, seed, 3, out=emb_out)
-        ops.embedding_bwd(ids, dy, dE, inp["scale"], p, seed, 3, zero_first=False)
-    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
 
-    def timeit(fn):
+    def cold(calls, reps=10):
+        """Mean time per call of one graph holding one call per rotated set."""
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for c in calls:
+                c()
+        g.replay()
+        torch.cuda.synchronize()
         a, b = ev(), ev()
         a.record()
-        for _ in range(iters):
-            fn()
+        for _ in range(reps):
+            g.replay()
         b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / iters * 1e3      # us
-    us_f = timeit(lambda: ops.embedding_fwd(ids, E, P, inp["scale"], p, seed, 3, out=emb_out))
-    us_b = timeit(lambda: ops.embedding_bwd(ids, dy, dE, inp["scale"], p, seed, 3, zero_first=False))
-    us_bz = timeit(lambda: ops.embedding_bwd(ids, dy, dE, inp["scale"], p, seed, 3, zero_first=True))
-    fwd_bytes = 4 * T + 2 * H * distinct + 2 * H * synth.C4.seq + 2 * T * H
-    bwd_bytes = 4 * T + 2 * T * H + 8 * H * distinct
-    out["embedding_fwd"] = {"shape": "ids [32,256], E [32768,1024]", "us": round(us_f, 2),
-                            "bytes": fwd_bytes, "GB/s": round(fwd_bytes / us_f / 1e3, 1)}
-    out["embedding_bwd"] = {"shape": "ids [32,256] -> dE [32768,1024] fp32 (accumulate, no zero-fill)",
-                            "us": round(us_b, 2), "bytes": bwd_bytes, "GB/s": round(bwd_bytes / us_b / 1e3, 1),
-                            "distinct_ids": distinct,
-                            "with_zero_fill_us": round(us_bz, 2)}
-    del ids, E, P, dy, emb_out, dE
+        return a.elapsed_time(b) * 1e3 / (reps * len(calls))
 
-    n = synth.C5_PARAMS
+    def row(shape, us, nbytes, **kw):
+        return {"shape": shape, "us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1), **kw}
+
+    # Elementwise backward, C3 shapes
+    T, H, F = synth.C3.tokens, synth.C3.hidden, synth.C3.ffn
     gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    rnd = lambda *s: torch.randn(*s, device="cuda", generator=gen).half()  # noqa: E731
+    calls = []
+    for _ in range(24):
+        dy, dx, db = rnd(T, H), torch.empty(T, H, dtype=torch.float16, device="cuda"), rnd(H)
+        ws = torch.empty(ops.elementwise_bwd_workspace_bytes(T, H), dtype=torch.uint8, device="cuda")
+        calls.append(lambda dy=dy, dx=dx, db=db, ws=ws: ops.bias_dropout_residual_bwd(
+            dy, p, seed, synth.SITE_FFN_OUT, dx=dx, dbias=db, workspace=ws))
+    nb = 4 * T * H + 2 * H
+    out["bias_dropout_residual_bwd"] = row(f"[{T},{H}] -> dx, dbias", cold(calls), nb)
+    del calls
+    fwd_out = ops.bias_relu_dropout(rnd(T, F), rnd(F), p, seed, synth.SITE_FFN_ACT)
+    calls = []
+    for _ in range(12):
+        dy, o, dx, db = rnd(T, F), fwd_out.clone(), torch.empty(T, F, dtype=torch.float16, device="cuda"), rnd(F)
+        ws = torch.empty(ops.elementwise_bwd_workspace_bytes(T, F), dtype=torch.uint8, device="cuda")
+        calls.append(lambda dy=dy, o=o, dx=dx, db=db, ws=ws: ops.bias_relu_dropout_bwd(
+            dy, o, p, dx=dx, dbias=db, workspace=ws))
+    nb = 6 * T * F + 2 * F
+    out["bias_relu_dropout_bwd"] = row(f"[{T},{F}] -> dx, dbias (from the forward output)", cold(calls), nb)
+    del calls, fwd_out
+    torch.cuda.empty_cache()
+
+    # Embedding, C4
+    inp = synth.embedding_inputs()
+    ids, P = d(inp["ids"]), d(inp["pos_emb"])
+    T4, H4 = inp["grad_out"].shape
+    V = inp["tok_emb"].shape[0]
+    distinct = int(np.unique(inp["ids"]).size)
+    s4 = inp["scale"]
+    calls = []
+    for _ in range(16):
+        E, o = d(inp["tok_emb"]), torch.empty((T4, H4), dtype=torch.float16, device="cuda")
+        calls.append(lambda E=E, o=o: ops.embedding_fwd(ids, E, P, s4, p, seed, synth.SITE_EMBEDDING, out=o))
+    nb = 4 * T4 + 2 * H4 * distinct + 2 * H4 * synth.C4.seq + 2 * T4 * H4
+    out["embedding_fwd"] = row(f"ids [{synth.C4.batch},{synth.C4.seq}], E [{V},{H4}]", cold(calls), nb,
+                               distinct_ids=distinct)
+    del calls
+    torch.cuda.empty_cache()
+    sets = [(d(inp["grad_out"]), torch.zeros((V, H4), dtype=torch.float32, device="cuda")) for _ in range(12)]
+    acc = [lambda dy=dy, dE=dE: ops.embedding_bwd(ids, dy, dE, s4, p, seed, synth.SITE_EMBEDDING, zero_first=False)
+           for dy, dE in sets]
+    zf = [lambda dy=dy, dE=dE: ops.embedding_bwd(ids, dy, dE, s4, p, seed, synth.SITE_EMBEDDING, zero_first=True)
+          for dy, dE in sets]
+    nb = 4 * T4 + 2 * T4 * H4 + 8 * H4 * distinct
+    out["embedding_bwd"] = row(f"ids [{synth.C4.batch},{synth.C4.seq}] -> dE [{V},{H4}] fp32 (accumulate)",
+                               cold(acc), nb, distinct_ids=distinct, with_zero_fill_us=round(cold(zf), 2))
+    del sets, acc, zf, ids, P
+    torch.cuda.empty_cache()
+
+    # Adam, 350M parameters (7.7 GB per step: larger than every cache by itself)
+    n = synth.C5_PARAMS
     gen.manual_seed(5)
     prm = (torch.randn(n, device="cuda", generator=gen) * 0.02).half()
     grd = (torch.randn(n, device="cuda", generator=gen) * 1e-3).half()
@@ -309,11 +356,16 @@ def extra_rows(torch, ops, iters=20):
                                 hp["weight_decay"], step[0], hp["grad_scale"], hp["decoupled_wd"])
     adam()
     torch.cuda.synchronize()
-    us_a = timeit(adam)
-    ab = 22 * n
-    out["adam_workspace_step"] = {"shape": "350M params, fp16 p/g, fp32 m/v, 1 launch", "us": round(us_a, 1),
-                                  "bytes": ab, "GB/s": round(ab / us_a / 1e3, 1),
-                                  "params_per_s": round(n / us_a * 1e6, 1)}
+    iters = 20
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(iters):
+        adam()
+    b.record()
+    torch.cuda.synchronize()
+    us_a = a.elapsed_time(b) / iters * 1e3
+    out["adam_workspace_step"] = row("350M params, fp16 p/g, fp32 m/v, 1 launch", us_a, 22 * n,
+                                     params_per_s=round(n / us_a * 1e6, 1))
     del prm, grd, m, v
     torch.cuda.empty_cache()
     return out

@@ -90,6 +90,37 @@ int ls_bias_dropout_residual(void* out, const void* x, const void* bias, const v
 int ls_bias_relu_dropout(void* out, const void* x, const void* bias, int64_t rows, int64_t cols,
                          float p, uint64_t seed, uint64_t offset, void* stream);
 
+/* Backward of the two operators above (their derivatives; [L10] technique 1
+ * and [LS2] sec. 2.1.1 fuse each operator in both directions).
+ *
+ * ls_bias_dropout_residual_bwd:
+ *     dx[r,c]   = dy[r,c] * keep(r*cols+c) / (1-p_eff)   (gradient of x and
+ *                 of the branch x + bias; the mask is regenerated from the
+ *                 forward's seed and offset)
+ *     dbias[c]  = sum_r dx[r,c]    (of the fp32 values, before rounding dx)
+ *     d_residual = dy: nothing is computed for it.
+ * ls_bias_relu_dropout_bwd:
+ *     dx[r,c]   = dy[r,c] * [out[r,c] > 0] / (1-p_eff),  dbias[c] = sum_r dx[r,c]
+ *   where out is the forward's output: for fp16 inputs out > 0 exactly when
+ *   the element was kept and x + bias > 0, so no random numbers are drawn;
+ *   p must be the forward's.
+ * dy, dx, out: fp16 [rows, cols]; dbias: fp16 [cols].  dx may alias dy (or
+ * out).  dbias is reduced in a fixed order (bit-reproducible).  rows == 0
+ * writes zeros to dbias; cols == 0 is a no-op.
+ * workspace: device memory of at least
+ * ls_elementwise_bwd_workspace_bytes(rows, cols) bytes (fp32 partial column
+ * sums), 16-byte aligned, not shared with a call that may run concurrently;
+ * its contents need no initialisation.  Errors: LS_ERR_WORKSPACE if too
+ * small; LS_ERR_PARAM for p outside [0, 1] or a misaligned workspace;
+ * LS_ERR_SHAPE for rows or cols >= 2^31. */
+size_t ls_elementwise_bwd_workspace_bytes(int64_t rows, int64_t cols);
+int ls_bias_dropout_residual_bwd(void* dx, void* dbias, const void* dy, int64_t rows, int64_t cols,
+                                 float p, uint64_t seed, uint64_t offset, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+int ls_bias_relu_dropout_bwd(void* dx, void* dbias, const void* dy, const void* out, int64_t rows,
+                             int64_t cols, float p, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* LayerNorm forward with one fused reduction pass ([L10] technique 2,
  * slide 21): per row, S1 = sum x and S2 = sum x^2 are reduced together;
  * mean = S1/H, var = max(S2/H - mean^2, 0), rstd = 1/sqrt(var + eps),

@@ -73,6 +73,46 @@ def bias_relu_dropout(x, bias, p, seed, offset, out=None):
     return out
 
 
+def elementwise_bwd_workspace_bytes(rows, cols):
+    return int(load().ls_elementwise_bwd_workspace_bytes(int(rows), int(cols)))
+
+
+def _ew_bwd_buffers(dy, dx, dbias, workspace):
+    rows, cols = _rows_cols(dy)
+    dx = torch.empty_like(dy) if dx is None else dx
+    dbias = torch.empty(cols, dtype=_F16, device=dy.device) if dbias is None else dbias
+    if workspace is None:
+        workspace = torch.empty(max(elementwise_bwd_workspace_bytes(rows, cols), 16), dtype=torch.uint8,
+                                device=dy.device)
+    return rows, cols, dx, dbias, workspace
+
+
+def bias_dropout_residual_bwd(dy, p, seed, offset, dx=None, dbias=None, workspace=None):
+    """Backward of bias_dropout_residual: returns (dx fp16, dbias fp16 [H]);
+    the residual's gradient is dy itself.  seed and offset are the forward's."""
+    _dev(dy, dx, dbias, workspace)
+    _dtype(dy, _F16, "dy")
+    rows, cols, dx, dbias, workspace = _ew_bwd_buffers(dy, dx, dbias, workspace)
+    check("ls_bias_dropout_residual_bwd", load().ls_bias_dropout_residual_bwd(
+        _ptr(dx), _ptr(dbias), _ptr(dy), rows, cols, float(p), int(seed), int(offset), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return dx, dbias
+
+
+def bias_relu_dropout_bwd(dy, out, p, dx=None, dbias=None, workspace=None):
+    """Backward of bias_relu_dropout from its output: returns (dx fp16, dbias fp16 [F])."""
+    _dev(dy, out, dx, dbias, workspace)
+    _dtype(dy, _F16, "dy")
+    _dtype(out, _F16, "out")
+    if out.shape != dy.shape:
+        raise ValueError("shape mismatch")
+    rows, cols, dx, dbias, workspace = _ew_bwd_buffers(dy, dx, dbias, workspace)
+    check("ls_bias_relu_dropout_bwd", load().ls_bias_relu_dropout_bwd(
+        _ptr(dx), _ptr(dbias), _ptr(dy), _ptr(out), rows, cols, float(p), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return dx, dbias
+
+
 def layernorm_fwd(x, gamma, beta, eps, y=None, mean=None, rstd=None):
     """Returns (y fp16, mean fp32 [rows], rstd fp32 [rows])."""
     _dev(x, gamma, beta, y, mean, rstd)

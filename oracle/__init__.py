@@ -36,7 +36,9 @@ from . import philox  # noqa: F401
 from .ops import (  # noqa: F401
     adam_workspace_step,
     bias_dropout_residual,
+    bias_dropout_residual_bwd,
     bias_relu_dropout,
+    bias_relu_dropout_bwd,
     dropout_keep,
     dropout_scale,
     embedding_bwd,

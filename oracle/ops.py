@@ -111,6 +111,41 @@ def bias_relu_dropout(x, bias, p, seed, offset, bits):
     return (ms * np.maximum(x64 + b64[None, :], 0.0)).astype(np.float16)
 
 
+def bias_dropout_residual_bwd(dy, p, seed, offset, bits):
+    """Gradients of out = residual + Dropout(x + bias) (the derivative of the
+    forward above; [L10] technique 1 and [LS2] sec. 2.1.1 fuse the operator in
+    both directions).
+
+    d_x = dy * keep * scale (also the gradient of the branch x + bias);
+    d_bias = the column sum of d_x over rows; d_residual = dy (not returned).
+    The mask is the forward's: same seed, offset and flat element index.
+    d_bias sums the unrounded float64 d_x; both are rounded once to fp16.
+    Returns (d_x fp16 [rows, cols], d_bias fp16 [cols]).
+    Parity: pinned by tests (torch autograd of the forward in float64; p = 0
+    gives d_x = dy; p = 1 gives zeros).
+    """
+    dy64 = np.asarray(dy, dtype=np.float64)
+    dx64 = dy64 * _masked_scale(dy64.shape, p, seed, offset, bits)
+    return dx64.astype(np.float16), dx64.sum(axis=0).astype(np.float16)
+
+
+def bias_relu_dropout_bwd(dy, x, bias, p, seed, offset, bits):
+    """Gradients of out = Dropout(ReLU(x + bias)) ([L10] slide 12's operator).
+
+    d_x = dy * keep * scale * [x + bias > 0] (ReLU's derivative taken as 0 at
+    0); d_bias = the column sum of d_x over rows.  Written from the forward's
+    inputs and mask; it needs no stored output.
+    Returns (d_x fp16 [rows, cols], d_bias fp16 [cols]).
+    Parity: pinned by tests (torch autograd of the forward in float64; the
+    gate equals [forward output > 0] for fp16 inputs; p = 0 is the plain ReLU
+    gradient).
+    """
+    dy64 = np.asarray(dy, dtype=np.float64)
+    pre = np.asarray(x, dtype=np.float64) + np.asarray(bias, dtype=np.float64)[None, :]
+    dx64 = dy64 * _masked_scale(dy64.shape, p, seed, offset, bits) * (pre > 0.0)
+    return dx64.astype(np.float16), dx64.sum(axis=0).astype(np.float16)
+
+
 # ----------------------------------------------------------------------------
 # LayerNorm ([L10] technique 2, slides 21-22)
 # ----------------------------------------------------------------------------

@@ -131,3 +131,22 @@ def test_probe_validation(lib):
     assert lib.ls_probe_read(None, FAKE, 1024, s) == LS_ERR_NULL
     assert lib.ls_probe_read(FAKE, FAKE, 1000, s) == LS_ERR_SHAPE
     assert lib.ls_probe_read(None, None, 0, s) == LS_OK
+
+
+def test_elementwise_bwd_validation(lib):
+    s = None
+    need = lib.ls_elementwise_bwd_workspace_bytes(4096, 768)
+    assert need > 0 and need % (768 * 4) == 0
+    assert lib.ls_elementwise_bwd_workspace_bytes(0, 768) == 0
+    assert lib.ls_elementwise_bwd_workspace_bytes(10, 0) == 0
+    a = (FAKE, FAKE, FAKE, 4096, 768)
+    assert lib.ls_bias_dropout_residual_bwd(*a, 0.1, 1, 0, FAKE, need - 1, s) == LS_ERR_WORKSPACE
+    assert lib.ls_bias_dropout_residual_bwd(*a, 0.1, 1, 0, None, need, s) == LS_ERR_NULL
+    assert lib.ls_bias_dropout_residual_bwd(*a, 0.1, 1, 0, ctypes.c_void_p(0x1008), need, s) == LS_ERR_PARAM
+    assert lib.ls_bias_dropout_residual_bwd(*a, 1.5, 1, 0, FAKE, need, s) == LS_ERR_PARAM
+    assert lib.ls_bias_dropout_residual_bwd(FAKE, None, FAKE, 4096, 768, 0.1, 1, 0, FAKE, need, s) == LS_ERR_NULL
+    assert lib.ls_bias_dropout_residual_bwd(FAKE, FAKE, FAKE, -1, 768, 0.1, 1, 0, FAKE, need, s) == LS_ERR_SHAPE
+    assert lib.ls_bias_dropout_residual_bwd(None, None, None, 5, 0, 0.1, 1, 0, None, 0, s) == LS_OK
+    assert lib.ls_bias_relu_dropout_bwd(FAKE, FAKE, FAKE, None, 4096, 768, 0.1, FAKE, need, s) == LS_ERR_NULL
+    assert lib.ls_bias_relu_dropout_bwd(FAKE, FAKE, FAKE, FAKE, 4096, 768, float("nan"), FAKE, need, s) == LS_ERR_PARAM
+    assert lib.ls_bias_relu_dropout_bwd(FAKE, FAKE, FAKE, FAKE, 4096, 768, 0.1, FAKE, need - 4, s) == LS_ERR_WORKSPACE

@@ -151,6 +151,73 @@ def test_nan_inf_propagate(ls):
 
 
 # ----------------------------------------------------------------------------
+# Backward of the fused elementwise operators
+# ----------------------------------------------------------------------------
+
+# full C3/C4 shapes, several 512-column segments with ragged last ones, the
+# element-wise path (cols % 8 != 0), one row, row counts that leave the last
+# row group short
+EW_BWD_SHAPES = [(4096, 768), (4096, 3072), (8192, 1024), (129, 520), (1000, 4104), (37, 24), (1, 8),
+                 (3, 13), (300, 20), (17, 1)]
+
+
+@pytest.mark.parametrize("rows,cols", EW_BWD_SHAPES)
+@pytest.mark.parametrize("p", [0.1, 0.0, 1.0])
+def test_bias_dropout_residual_bwd(ls, rows, cols, p):
+    g = np.random.default_rng(rows * 7919 + cols)
+    dy = synth.normal16(g, (rows, cols), 1.0)
+    dx, db = ls.bias_dropout_residual_bwd(dev(dy), p, SEED, synth.SITE_FFN_OUT)
+    what = f"bias_dropout_residual_bwd {rows}x{cols} p={p} [{last_dispatch()}]"
+    ref_dx, ref_db = oracle.bias_dropout_residual_bwd(dy, p, SEED, synth.SITE_FFN_OUT, BITS)
+    assert_fp16(host(dx), ref_dx, what + " dx")
+    assert_fp16(host(db), ref_db, what + " dbias")
+
+
+@pytest.mark.parametrize("rows,cols", EW_BWD_SHAPES)
+def test_bias_relu_dropout_bwd_after_forward(ls, rows, cols):
+    """GPU forward, then GPU backward from its output, against the oracle's
+    backward written from the forward's inputs and mask."""
+    g = np.random.default_rng(rows * 104729 + cols)
+    x = synth.normal16(g, (rows, cols), 1.0)
+    b = synth.normal16(g, (cols,), 0.02)
+    dy = synth.normal16(g, (rows, cols), 1.0)
+    p = 0.1
+    out = ls.bias_relu_dropout(dev(x), dev(b), p, SEED, synth.SITE_FFN_ACT)
+    dx, db = ls.bias_relu_dropout_bwd(dev(dy), out, p)
+    what = f"bias_relu_dropout_bwd {rows}x{cols} [{last_dispatch()}]"
+    ref_dx, ref_db = oracle.bias_relu_dropout_bwd(dy, x, b, p, SEED, synth.SITE_FFN_ACT, BITS)
+    assert_fp16(host(dx), ref_dx, what + " dx")
+    assert_fp16(host(db), ref_db, what + " dbias")
+
+
+def test_ew_bwd_dispatch_alias_determinism_and_empty(ls):
+    g = np.random.default_rng(5)
+    dy = synth.normal16(g, (4096, 3072), 1.0)
+    ref_dx, ref_db = oracle.bias_dropout_residual_bwd(dy, 0.1, SEED, 1, BITS)
+    t = dev(dy)
+    dx, db = ls.bias_dropout_residual_bwd(t, 0.1, SEED, 1, dx=t)          # in place
+    assert last_dispatch().startswith("bias_dropout_residual_bwd/seg512_w16_g")
+    assert_fp16(host(dx), ref_dx, "in-place dx")
+    db2 = ls.bias_dropout_residual_bwd(dev(dy), 0.1, SEED, 1)[1]
+    assert np.array_equal(host(db).view(np.uint16), host(db2).view(np.uint16))   # fixed order
+    assert_fp16(host(db2), ref_db, "dbias")
+    # the forward output may be overwritten by the gradient
+    x = synth.normal16(g, (64, 768), 1.0)
+    b = synth.normal16(g, (768,), 0.02)
+    dy2 = synth.normal16(g, (64, 768), 1.0)
+    out = ls.bias_relu_dropout(dev(x), dev(b), 0.1, SEED, 1)
+    dx3, _ = ls.bias_relu_dropout_bwd(dev(dy2), out, 0.1, dx=out)
+    assert_fp16(host(dx3), oracle.bias_relu_dropout_bwd(dy2, x, b, 0.1, SEED, 1, BITS)[0], "dx over out")
+    # no rows: dbias is zero; no columns: nothing to do
+    empty = torch.empty((0, 40), dtype=torch.float16, device="cuda")
+    dbz = torch.full((40,), 3.0, dtype=torch.float16, device="cuda")
+    ls.bias_dropout_residual_bwd(empty, 0.1, SEED, 1, dbias=dbz)
+    assert (host(dbz) == 0).all()
+    ls.bias_relu_dropout_bwd(empty, empty, 0.1, dbias=dbz)
+    assert (host(dbz) == 0).all()
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
 

@@ -76,6 +76,83 @@ def test_dropout_all_dropped():
     assert (out == 1).all()
 
 
+def test_bdr_bwd_torch_autograd_and_special_cases():
+    """Autograd of residual + m * (x + b) in float64 gives d_x, d_bias and
+    d_residual = dy; p = 0 passes dy through; p = 1 gives zeros; the backward's
+    mask is the forward's (same flat index)."""
+    g = np.random.default_rng(21)
+    rows, cols, p, off = 29, 40, 0.5, 4      # scale 2: every float64 sum below is exact
+    x, r, dy = (f16(g.normal(size=(rows, cols))) for _ in range(3))
+    b = f16(g.normal(0, 0.02, size=cols))
+    keep = dropout_keep(rows * cols, p, SEED, off, BITS).reshape(rows, cols)
+    m = torch.tensor(keep * dropout_scale(p, BITS))
+    xt, bt, rt = (torch.tensor(a.astype(np.float64), requires_grad=True) for a in (x, b, r))
+    (rt + m * (xt + bt)).backward(torch.tensor(dy.astype(np.float64)))
+    dx, db = oracle.bias_dropout_residual_bwd(dy, p, SEED, off, BITS)
+    np.testing.assert_array_equal(dx, xt.grad.numpy().astype(np.float16))
+    np.testing.assert_array_equal(db, bt.grad.numpy().astype(np.float16))
+    np.testing.assert_array_equal(rt.grad.numpy(), dy.astype(np.float64))
+    dx0, db0 = oracle.bias_dropout_residual_bwd(dy, 0.0, SEED, off, BITS)
+    np.testing.assert_array_equal(dx0, dy)
+    np.testing.assert_array_equal(db0, dy.astype(np.float64).sum(0).astype(np.float16))
+    dx1, db1 = oracle.bias_dropout_residual_bwd(dy, 1.0, SEED, off, BITS)
+    assert (dx1 == 0).all() and (db1 == 0).all()
+    ones = np.ones((rows, cols), np.float16)
+    fwd = oracle.bias_dropout_residual(ones, np.zeros(cols, np.float16), np.zeros_like(ones), p, SEED, off, BITS)
+    np.testing.assert_array_equal(oracle.bias_dropout_residual_bwd(ones, p, SEED, off, BITS)[0], fwd)
+
+
+def test_brd_bwd_torch_autograd_and_output_gate():
+    """Autograd of m * relu(x + b) in float64; the gate [x + b > 0] * keep equals
+    [forward output > 0] for fp16 inputs, including x + b = 0 and the smallest
+    positive fp16 subnormal."""
+    g = np.random.default_rng(22)
+    rows, cols, p, off = 31, 48, 0.5, 1      # scale 2: every float64 sum below is exact
+    x = f16(g.normal(size=(rows, cols)))
+    b = f16(g.normal(0, 0.5, size=cols))
+    b[:4] = 0
+    x[:, 0] = 0                                        # pre = 0: ReLU's derivative 0
+    x[:, 1] = np.float16(2.0 ** -24)                   # smallest positive pre
+    x[:, 2] = -b[2]
+    x[:, 5] = -b[5]                                    # pre = 0 with b != 0
+    dy = f16(g.normal(size=(rows, cols)))
+    keep = dropout_keep(rows * cols, p, SEED, off, BITS).reshape(rows, cols)
+    m = torch.tensor(keep * dropout_scale(p, BITS))
+    xt, bt = (torch.tensor(a.astype(np.float64), requires_grad=True) for a in (x, b))
+    (m * torch.relu(xt + bt)).backward(torch.tensor(dy.astype(np.float64)))
+    dx, db = oracle.bias_relu_dropout_bwd(dy, x, b, p, SEED, off, BITS)
+    np.testing.assert_array_equal(dx, xt.grad.numpy().astype(np.float16))
+    np.testing.assert_array_equal(db, bt.grad.numpy().astype(np.float16))
+    out = oracle.bias_relu_dropout(x, b, p, SEED, off, BITS)
+    gate = (out.astype(np.float64) > 0) * dropout_scale(p, BITS)
+    np.testing.assert_array_equal(dx, (dy.astype(np.float64) * gate).astype(np.float16))
+    assert (out[:, 1] > 0).any() and (dx[:, 0] == 0).all() and (dx[:, 5] == 0).all()
+    dx0, _ = oracle.bias_relu_dropout_bwd(dy, x, b, 0.0, SEED, off, BITS)
+    pre = x.astype(np.float64) + b.astype(np.float64)
+    np.testing.assert_array_equal(dx0, np.where(pre > 0, dy, np.float16(0)))
+
+
+def test_ew_bwd_inexact_scale_within_one_ulp():
+    """With p = 0.25 (scale 4/3, inexact in binary) d_x is still exact per
+    element, and d_bias can sit on an fp16 rounding tie whose side depends on
+    float64 summation order: it agrees with autograd to one fp16 ulp."""
+    g = np.random.default_rng(23)
+    rows, cols, p, off = 31, 48, 0.25, 1
+    x, dy = f16(g.normal(size=(rows, cols))), f16(g.normal(size=(rows, cols)))
+    b = f16(g.normal(0, 0.5, size=cols))
+    keep = dropout_keep(rows * cols, p, SEED, off, BITS).reshape(rows, cols)
+    m = torch.tensor(keep * dropout_scale(p, BITS))
+    for relu in (False, True):
+        xt, bt = (torch.tensor(a.astype(np.float64), requires_grad=True) for a in (x, b))
+        y = m * (torch.relu(xt + bt) if relu else (xt + bt))
+        y.backward(torch.tensor(dy.astype(np.float64)))
+        dx, db = (oracle.bias_relu_dropout_bwd(dy, x, b, p, SEED, off, BITS) if relu
+                  else oracle.bias_dropout_residual_bwd(dy, p, SEED, off, BITS))
+        np.testing.assert_array_equal(dx, xt.grad.numpy().astype(np.float16))
+        ref = bt.grad.numpy()
+        np.testing.assert_allclose(db.astype(np.float64), ref, rtol=2.0 ** -10, atol=2.0 ** -24)
+
+
 # ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
