@@ -313,6 +313,22 @@ def extra_rows(torch, ops):
     del calls, fwd_out
     torch.cuda.empty_cache()
 
+    # Bias + Q/K/V head split and its backward, C3 attention shape
+    B, L, NH = synth.C3.batch, synth.C3.seq, synth.C3.heads
+    H3 = 3 * H
+    calls, bcalls = [], []
+    for _ in range(24):
+        qkv, bias, o = rnd(T, H3), rnd(H3), torch.empty((3, B, NH, L, H // NH), dtype=torch.float16, device="cuda")
+        calls.append(lambda qkv=qkv, bias=bias, o=o: ops.bias_qkv_split(qkv, bias, B, L, NH, out=o))
+        dq, db = torch.empty(T, H3, dtype=torch.float16, device="cuda"), rnd(H3)
+        ws = torch.empty(ops.elementwise_bwd_workspace_bytes(T, H3), dtype=torch.uint8, device="cuda")
+        bcalls.append(lambda o=o, dq=dq, db=db, ws=ws: ops.bias_qkv_split_bwd(o, dqkv=dq, dbias=db, workspace=ws))
+    shape = f"[{T},{H3}] <-> 3 x [{B},{NH},{L},{H // NH}]"
+    out["bias_qkv_split"] = row(shape, cold(calls), 4 * T * H3 + 2 * H3)
+    out["bias_qkv_split_bwd"] = row(shape + " + dbias", cold(bcalls), 4 * T * H3 + 2 * H3)
+    del calls, bcalls
+    torch.cuda.empty_cache()
+
     # Embedding, C4
     inp = synth.embedding_inputs()
     ids, P = d(inp["ids"]), d(inp["pos_emb"])

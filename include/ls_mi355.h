@@ -121,6 +121,35 @@ int ls_bias_relu_dropout_bwd(void* dx, void* dbias, const void* dy, const void* 
                              int64_t cols, float p, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Bias add fused with the split of the Q/K/V projection into heads, and its
+ * inverse for the backward ([L10] technique 1, slide 12; [LS2] sec. 2.1.1
+ * lists it with the fused elementwise kernels of the attention block).
+ * T = batch * seq_len tokens, H = heads * head_dim.
+ *
+ * ls_bias_qkv_split:
+ *     out[k][b][h][l][j] = qkv[b*seq_len + l][k*H + h*head_dim + j]
+ *                          + bias[k*H + h*head_dim + j]
+ *   qkv: fp16 [T, 3H], each token row holding its Q, K and V parts in that
+ *   order, each part heads x head_dim; bias: fp16 [3H];
+ *   out: fp16 [3, batch, heads, seq_len, head_dim] (Q, K, V, one contiguous
+ *   [seq_len, head_dim] tile per head).  No aliasing.
+ * ls_bias_qkv_split_bwd:
+ *     dqkv[b*seq_len + l][k*H + h*head_dim + j] = dout[k][b][h][l][j]
+ *     dbias[c] = sum over tokens of dqkv[t][c]   (fp32, fixed order)
+ *   dout: fp16 [3, batch, heads, seq_len, head_dim]; dqkv: fp16 [T, 3H]
+ *   (an exact permutation of dout); dbias: fp16 [3H].  No aliasing.
+ *   workspace: at least ls_elementwise_bwd_workspace_bytes(T, 3H) bytes,
+ *   16-byte aligned, not shared with a concurrent call; no initialisation.
+ *   T == 0 writes zeros to dbias; H == 0 is a no-op.
+ * head_dim % 8 == 0 with 16-byte aligned pointers takes the vector path.
+ * Errors: LS_ERR_SHAPE for negative or too large sizes, LS_ERR_NULL,
+ * LS_ERR_WORKSPACE, LS_ERR_PARAM for a misaligned workspace. */
+int ls_bias_qkv_split(void* out, const void* qkv, const void* bias, int64_t batch, int64_t seq_len,
+                      int64_t heads, int64_t head_dim, void* stream);
+int ls_bias_qkv_split_bwd(void* dqkv, void* dbias, const void* dout, int64_t batch, int64_t seq_len,
+                          int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* LayerNorm forward with one fused reduction pass ([L10] technique 2,
  * slide 21): per row, S1 = sum x and S2 = sum x^2 are reduced together;
  * mean = S1/H, var = max(S2/H - mean^2, 0), rstd = 1/sqrt(var + eps),

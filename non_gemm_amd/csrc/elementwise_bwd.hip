@@ -17,38 +17,16 @@
 // block fold their sums through LDS in wave order, the block writes one
 // partial row, and a second kernel sums the partial rows column by column in
 // a fixed order, so d_bias is bit-reproducible.
-#include "ls_common.hpp"
+#include "colsum.hpp"
 
 namespace ls {
 namespace {
 
-constexpr int kWavesPerBlock = 16;
-constexpr int kBwdBlock = kWavesPerBlock * kWave;      // 1024 threads
-constexpr int kSegVecs = kWave;                        // 64 vectors = 512 columns per segment
-constexpr int kSegCols = kSegVecs * 8;
-constexpr int kMaxGroups = 256;
-constexpr int kTargetWaves = 6144;                     // ~24 per CU: enough loads in flight
-
-// Row groups: as many as keep ~kTargetWaves waves busy, at most one per 16
-// rows (every wave gets a row) and at most kMaxGroups (the finalisation reads
-// at most 16 partial rows per thread).  Depends on the shape only, so the
-// workspace size is known before the pointers are.
-uint32_t bwd_groups(int64_t rows, int64_t cols) {
-    if (rows <= 0 || cols <= 0) return 0;
-    const int64_t segs = (cols + kSegCols - 1) / kSegCols;
-    int64_t g = (kTargetWaves + kWavesPerBlock * segs - 1) / (kWavesPerBlock * segs);
-    const int64_t by_rows = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (g > by_rows) g = by_rows;
-    if (g > kMaxGroups) g = kMaxGroups;
-    return static_cast<uint32_t>(g < 1 ? 1 : g);
-}
-
 template <bool RELU>
-__global__ __launch_bounds__(kBwdBlock) void ew_bwd_vec_kernel(half8* dx, float* partial, const half8* dy,
+__global__ __launch_bounds__(kCsBlock) void ew_bwd_vec_kernel(half8* dx, float* partial, const half8* dy,
                                                                const half8* out, uint32_t rows,
                                                                uint32_t nv, uint32_t rows_per_group,
                                                                Dropout d) {
-    __shared__ float4v fold[kWavesPerBlock][2][kSegVecs];   // 32 KiB: [wave][half][lane]
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const uint32_t cv = blockIdx.x * kSegVecs + lane;        // this lane's vector column
@@ -67,8 +45,8 @@ __global__ __launch_bounds__(kBwdBlock) void ew_bwd_vec_kernel(half8* dx, float*
         gy = __builtin_nontemporal_load(dy + v);
         if (RELU) go = __builtin_nontemporal_load(out + v);
     }
-    for (; r < r_end; r += kWavesPerBlock) {
-        const uint32_t rn = r + kWavesPerBlock;
+    for (; r < r_end; r += kCsWaves) {
+        const uint32_t rn = r + kCsWaves;
         half8 ny{}, no{};
         if (col_ok && rn < r_end) {                          // next row's loads first
             const size_t v = static_cast<size_t>(rn) * nv + cv;
@@ -98,21 +76,7 @@ __global__ __launch_bounds__(kBwdBlock) void ew_bwd_vec_kernel(half8* dx, float*
         go = no;
     }
 
-    fold[wave][0][lane] = float4v{acc[0], acc[1], acc[2], acc[3]};
-    fold[wave][1][lane] = float4v{acc[4], acc[5], acc[6], acc[7]};
-    __syncthreads();
-    // Thread t < 512 sums column t of the segment over the 16 waves in order.
-    if (threadIdx.x < kSegCols) {
-        const int c = threadIdx.x;
-        const int l = c >> 3, k = c & 7;
-        const uint32_t col = blockIdx.x * kSegCols + c;
-        if (col < nv * 8u) {
-            float t = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kWavesPerBlock; ++w) t += fold[w][k >> 2][l][k & 3];
-            partial[static_cast<size_t>(blockIdx.y) * nv * 8u + col] = t;
-        }
-    }
+    colsum_block_fold(partial, acc, nv * 8u);
 }
 
 // Element-wise path (cols % 8 != 0 or unaligned tensors): thread = one column
@@ -136,37 +100,6 @@ __global__ __launch_bounds__(256) void ew_bwd_scalar_kernel(half_t* dx, float* p
     partial[static_cast<size_t>(blockIdx.y) * cols + c] = acc;
 }
 
-// d_bias[c] = sum over the partial rows g = 0..ngroups-1 of partial[g][c]:
-// 16 thread slices per column (slice s takes rows s, s+16, ...), then the 16
-// slice sums in order.  ngroups == 0 writes zeros (no rows).
-constexpr int kFinCols = 16;
-constexpr int kFinSlices = 16;
-static_assert(kFinSlices * 16 >= kMaxGroups, "16 loads per thread cover every partial row");
-
-__global__ __launch_bounds__(kFinCols * kFinSlices) void colsum_finalize_kernel(half_t* dbias, const float* partial,
-                                                                             uint32_t ngroups, uint32_t cols) {
-    __shared__ float sums[kFinSlices][kFinCols];
-    const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
-    const uint32_t c = blockIdx.x * kFinCols + cl;
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t g = sl + i * kFinSlices;
-        v[i] = (c < cols && g < ngroups) ? partial[static_cast<size_t>(g) * cols + c] : 0.0f;
-    }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a += v[i];
-    sums[sl][cl] = a;
-    __syncthreads();
-    if (sl == 0 && c < cols) {
-        float t = 0.0f;
-#pragma unroll
-        for (int s = 0; s < kFinSlices; ++s) t += sums[s][cl];
-        dbias[c] = static_cast<half_t>(t);
-    }
-}
-
 template <bool RELU>
 int launch_bwd(const char* name, void* dx, void* dbias, const void* dy, const void* out, int64_t rows,
                int64_t cols, float p, uint64_t seed, uint64_t offset, void* workspace,
@@ -183,21 +116,15 @@ int launch_bwd(const char* name, void* dx, void* dbias, const void* dy, const vo
     if (!dbias) return fail(LS_ERR_NULL, "%s: null dbias", name);
     if (cols >= (1ll << 31) || rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: shape too large", name);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const unsigned fgrid = static_cast<unsigned>((cols + kFinCols - 1) / kFinCols);
     clear_hip_error();
     if (rows == 0) {                                   // no rows: d_bias is zero
-        colsum_finalize_kernel<<<fgrid, kFinCols * kFinSlices, 0, s>>>(static_cast<half_t*>(dbias), nullptr, 0,
-                                                                       static_cast<uint32_t>(cols));
+        colsum_finalize(static_cast<half_t*>(dbias), nullptr, 0, static_cast<uint32_t>(cols), s);
         set_dispatch(RELU ? "bias_relu_dropout_bwd/empty_rows" : "bias_dropout_residual_bwd/empty_rows");
         return launch_status(name);
     }
     if (!dx || !dy || (RELU && !out)) return fail(LS_ERR_NULL, "%s: null tensor pointer", name);
-    const uint32_t groups = bwd_groups(rows, cols);
-    const size_t need = static_cast<size_t>(groups) * static_cast<size_t>(cols) * sizeof(float);
-    if (!workspace) return fail(LS_ERR_NULL, "%s: null workspace", name);
-    if (workspace_bytes < need)
-        return fail(LS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", name, workspace_bytes, need);
-    if (!aligned16(workspace)) return fail(LS_ERR_PARAM, "%s: workspace must be 16-byte aligned", name);
+    if (int rc = colsum_check_workspace(name, workspace, workspace_bytes, rows, cols)) return rc;
+    const uint32_t groups = colsum_groups(rows, cols);
     float* part = static_cast<float*>(workspace);
     const uint64_t rpg = (static_cast<uint64_t>(rows) + groups - 1) / groups;
     const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols);
@@ -207,7 +134,7 @@ int launch_bwd(const char* name, void* dx, void* dbias, const void* dy, const vo
     if (vec) {
         const uint32_t nv = static_cast<uint32_t>(cols / 8);
         const dim3 grid((nv + kSegVecs - 1) / kSegVecs, groups);
-        ew_bwd_vec_kernel<RELU><<<grid, kBwdBlock, 0, s>>>(static_cast<half8*>(dx), part,
+        ew_bwd_vec_kernel<RELU><<<grid, kCsBlock, 0, s>>>(static_cast<half8*>(dx), part,
                                                            static_cast<const half8*>(dy),
                                                            static_cast<const half8*>(out),
                                                            static_cast<uint32_t>(rows), nv,
@@ -226,8 +153,7 @@ int launch_bwd(const char* name, void* dx, void* dbias, const void* dy, const vo
     }
     int rc = launch_status(name);
     if (rc != LS_OK) return rc;
-    colsum_finalize_kernel<<<fgrid, kFinCols * kFinSlices, 0, s>>>(static_cast<half_t*>(dbias), part, groups,
-                                                                   static_cast<uint32_t>(cols));
+    colsum_finalize(static_cast<half_t*>(dbias), part, groups, static_cast<uint32_t>(cols), s);
     set_dispatch(buf);
     return launch_status(name);
 }
@@ -239,7 +165,7 @@ extern "C" {
 
 size_t ls_elementwise_bwd_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0 || cols >= (1ll << 31) || rows >= (1ll << 31)) return 0;
-    return static_cast<size_t>(ls::bwd_groups(rows, cols)) * static_cast<size_t>(cols) * sizeof(float);
+    return ls::colsum_workspace_bytes(rows, cols);
 }
 
 int ls_bias_dropout_residual_bwd(void* dx, void* dbias, const void* dy, int64_t rows, int64_t cols, float p,

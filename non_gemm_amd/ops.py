@@ -113,6 +113,40 @@ def bias_relu_dropout_bwd(dy, out, p, dx=None, dbias=None, workspace=None):
     return dx, dbias
 
 
+def bias_qkv_split(qkv, bias, batch, seq_len, heads, out=None):
+    """qkv [batch*seq_len, 3H] fp16 + bias [3H] -> [3, batch, heads, seq_len, head_dim]."""
+    _dev(qkv, bias, out)
+    _dtype(qkv, _F16, "qkv")
+    _dtype(bias, _F16, "bias")
+    tokens, cols = _rows_cols(qkv)
+    if tokens != batch * seq_len or cols % (3 * heads) or bias.shape != (cols,):
+        raise ValueError("shape mismatch")
+    d = cols // (3 * heads)
+    out = torch.empty((3, batch, heads, seq_len, d), dtype=_F16, device=qkv.device) if out is None else out
+    check("ls_bias_qkv_split", load().ls_bias_qkv_split(
+        _ptr(out), _ptr(qkv), _ptr(bias), int(batch), int(seq_len), int(heads), int(d), _stream()))
+    return out
+
+
+def bias_qkv_split_bwd(dout, dqkv=None, dbias=None, workspace=None):
+    """dout [3, batch, heads, seq_len, head_dim] -> (dqkv [batch*seq_len, 3H], dbias [3H])."""
+    _dev(dout, dqkv, dbias, workspace)
+    _dtype(dout, _F16, "dout")
+    if dout.dim() != 5 or dout.shape[0] != 3:
+        raise ValueError("dout must be [3, batch, heads, seq_len, head_dim]")
+    _, b, h, l, d = dout.shape
+    tokens, cols = b * l, 3 * h * d
+    dqkv = torch.empty((tokens, cols), dtype=_F16, device=dout.device) if dqkv is None else dqkv
+    dbias = torch.empty(cols, dtype=_F16, device=dout.device) if dbias is None else dbias
+    if workspace is None:
+        workspace = torch.empty(max(elementwise_bwd_workspace_bytes(tokens, cols), 16), dtype=torch.uint8,
+                                device=dout.device)
+    check("ls_bias_qkv_split_bwd", load().ls_bias_qkv_split_bwd(
+        _ptr(dqkv), _ptr(dbias), _ptr(dout), int(b), int(l), int(h), int(d), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return dqkv, dbias
+
+
 def layernorm_fwd(x, gamma, beta, eps, y=None, mean=None, rstd=None):
     """Returns (y fp16, mean fp32 [rows], rstd fp32 [rows])."""
     _dev(x, gamma, beta, y, mean, rstd)

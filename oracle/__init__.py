@@ -37,6 +37,8 @@ from .ops import (  # noqa: F401
     adam_workspace_step,
     bias_dropout_residual,
     bias_dropout_residual_bwd,
+    bias_qkv_split,
+    bias_qkv_split_bwd,
     bias_relu_dropout,
     bias_relu_dropout_bwd,
     dropout_keep,

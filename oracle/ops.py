@@ -147,6 +147,41 @@ def bias_relu_dropout_bwd(dy, x, bias, p, seed, offset, bits):
 
 
 # ----------------------------------------------------------------------------
+# Bias add + Q/K/V head split ([L10] technique 1, slide 12; [LS2] sec. 2.1.1)
+# ----------------------------------------------------------------------------
+
+
+def bias_qkv_split(qkv, bias, batch, seq_len, heads):
+    """out[k, b, h, l, j] = qkv[b*L + l, k*H + h*d + j] + bias[k*H + h*d + j].
+
+    qkv: fp16 [T, 3H] with T = batch * seq_len, each token row holding its Q,
+    K and V parts in that order, each part heads x d (the layout of one
+    fused [H, 3H] projection); bias: fp16 [3H].  Returns fp16
+    [3, batch, heads, seq_len, d]: one contiguous [seq_len, d] tile per
+    head.  The sum is rounded once to fp16.
+    Parity: pinned by tests (brute-force index loops; zero bias is an exact
+    permutation undone by the backward).
+    """
+    x = np.asarray(qkv, dtype=np.float64) + np.asarray(bias, dtype=np.float64)[None, :]
+    tokens, cols = x.shape
+    d = cols // (3 * heads)
+    y = x.reshape(batch, seq_len, 3, heads, d).transpose(2, 0, 3, 1, 4)
+    return np.ascontiguousarray(y).astype(np.float16)
+
+
+def bias_qkv_split_bwd(dout, batch, seq_len, heads):
+    """Gradients of bias_qkv_split: dqkv [T, 3H] is dout put back in the
+    projection's layout (the inverse permutation, exact) and dbias [3H] is
+    the column sum of dqkv over tokens, rounded once to fp16.
+    Parity: pinned by tests (torch autograd of the forward; brute force).
+    """
+    g = np.asarray(dout, dtype=np.float64)
+    three, b, h, l, d = g.shape
+    dq = np.ascontiguousarray(g.transpose(1, 3, 0, 2, 4)).reshape(b * l, 3 * h * d)
+    return dq.astype(np.float16), dq.sum(axis=0).astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm ([L10] technique 2, slides 21-22)
 # ----------------------------------------------------------------------------
 

@@ -150,3 +150,16 @@ def test_elementwise_bwd_validation(lib):
     assert lib.ls_bias_relu_dropout_bwd(FAKE, FAKE, FAKE, None, 4096, 768, 0.1, FAKE, need, s) == LS_ERR_NULL
     assert lib.ls_bias_relu_dropout_bwd(FAKE, FAKE, FAKE, FAKE, 4096, 768, float("nan"), FAKE, need, s) == LS_ERR_PARAM
     assert lib.ls_bias_relu_dropout_bwd(FAKE, FAKE, FAKE, FAKE, 4096, 768, 0.1, FAKE, need - 4, s) == LS_ERR_WORKSPACE
+
+
+def test_qkv_split_validation(lib):
+    s = None
+    assert lib.ls_bias_qkv_split(FAKE, FAKE, FAKE, -1, 128, 12, 64, s) == LS_ERR_SHAPE
+    assert lib.ls_bias_qkv_split(FAKE, None, FAKE, 32, 128, 12, 64, s) == LS_ERR_NULL
+    assert lib.ls_bias_qkv_split(None, None, None, 0, 128, 12, 64, s) == LS_OK
+    assert lib.ls_bias_qkv_split(FAKE, FAKE, FAKE, 1 << 31, 1 << 31, 1 << 20, 1 << 20, s) == LS_ERR_SHAPE
+    need = lib.ls_elementwise_bwd_workspace_bytes(4096, 2304)
+    assert lib.ls_bias_qkv_split_bwd(FAKE, FAKE, FAKE, 32, 128, 12, 64, FAKE, need - 1, s) == LS_ERR_WORKSPACE
+    assert lib.ls_bias_qkv_split_bwd(FAKE, None, FAKE, 32, 128, 12, 64, FAKE, need, s) == LS_ERR_NULL
+    assert lib.ls_bias_qkv_split_bwd(FAKE, FAKE, None, 32, 128, 12, 64, FAKE, need, s) == LS_ERR_NULL
+    assert lib.ls_bias_qkv_split_bwd(None, None, None, 32, 128, 0, 64, None, 0, s) == LS_OK

@@ -218,6 +218,44 @@ def test_ew_bwd_dispatch_alias_determinism_and_empty(ls):
 
 
 # ----------------------------------------------------------------------------
+# Bias + Q/K/V head split and its backward (exact permutation: bit-exact)
+# ----------------------------------------------------------------------------
+
+# BERT-base (C3) and Transformer-big (C4) attention shapes, ragged segment
+# counts, head_dim not a multiple of 8 (element-wise path), one token
+QKV_SHAPES = [(32, 128, 12, 64), (32, 256, 16, 64), (3, 7, 5, 24), (2, 9, 3, 12), (1, 1, 1, 8), (4, 33, 2, 40)]
+
+
+@pytest.mark.parametrize("batch,seq,heads,d", QKV_SHAPES)
+def test_bias_qkv_split(ls, batch, seq, heads, d):
+    g = np.random.default_rng(batch * 1009 + seq * 31 + heads * 7 + d)
+    qkv = synth.normal16(g, (batch * seq, 3 * heads * d), 1.0)
+    bias = synth.normal16(g, (3 * heads * d,), 0.02)
+    out = host(ls.bias_qkv_split(dev(qkv), dev(bias), batch, seq, heads))
+    what = f"bias_qkv_split {batch}x{seq}x{heads}x{d} [{last_dispatch()}]"
+    ref = oracle.bias_qkv_split(qkv, bias, batch, seq, heads)
+    assert np.array_equal(out.view(np.uint16), ref.view(np.uint16)), what
+    dout = synth.normal16(g, ref.shape, 1.0)
+    dq, db = ls.bias_qkv_split_bwd(dev(dout))
+    what = f"bias_qkv_split_bwd {batch}x{seq}x{heads}x{d} [{last_dispatch()}]"
+    ref_dq, ref_db = oracle.bias_qkv_split_bwd(dout, batch, seq, heads)
+    assert np.array_equal(host(dq).view(np.uint16), ref_dq.view(np.uint16)), what
+    assert_fp16(host(db), ref_db, what + " dbias")
+
+
+def test_bias_qkv_split_dispatch_and_empty(ls):
+    g = np.random.default_rng(3)
+    qkv = dev(synth.normal16(g, (4096, 2304), 1.0))
+    ls.bias_qkv_split(qkv, dev(synth.normal16(g, (2304,), 0.02)), 32, 128, 12)
+    assert last_dispatch() == "bias_qkv_split/vec8"
+    ls.bias_qkv_split_bwd(dev(synth.normal16(g, (3, 32, 12, 128, 64), 1.0)))
+    assert last_dispatch().startswith("bias_qkv_split_bwd/seg512_w16_g")
+    dbz = torch.full((3 * 2 * 8,), 5.0, dtype=torch.float16, device="cuda")
+    ls.bias_qkv_split_bwd(torch.empty((3, 0, 2, 4, 8), dtype=torch.float16, device="cuda"), dbias=dbz)
+    assert (host(dbz) == 0).all()
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
 

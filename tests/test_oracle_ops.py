@@ -154,6 +154,58 @@ def test_ew_bwd_inexact_scale_within_one_ulp():
 
 
 # ----------------------------------------------------------------------------
+# Bias + Q/K/V head split
+# ----------------------------------------------------------------------------
+
+def test_qkv_split_brute_force():
+    """Every output element against its defining index formula, loop by loop."""
+    g = np.random.default_rng(31)
+    batch, seq, heads, d = 2, 3, 2, 4
+    H = heads * d
+    qkv = f16(g.normal(size=(batch * seq, 3 * H)))
+    bias = f16(g.normal(size=3 * H))
+    out = oracle.bias_qkv_split(qkv, bias, batch, seq, heads)
+    assert out.shape == (3, batch, heads, seq, d)
+    for k in range(3):
+        for b in range(batch):
+            for h in range(heads):
+                for l in range(seq):
+                    for j in range(d):
+                        c = k * H + h * d + j
+                        want = np.float16(float(qkv[b * seq + l, c]) + float(bias[c]))
+                        assert out[k, b, h, l, j] == want
+    dout = f16(g.normal(size=out.shape))
+    dq, db = oracle.bias_qkv_split_bwd(dout, batch, seq, heads)
+    for k in range(3):
+        for b in range(batch):
+            for h in range(heads):
+                for l in range(seq):
+                    for j in range(d):
+                        assert dq[b * seq + l, k * H + h * d + j] == dout[k, b, h, l, j]
+    for c in range(3 * H):
+        k, h, j = c // H, (c % H) // d, c % d
+        assert db[c] == np.float16(sum(float(dout[k, b, h, l, j]) for b in range(batch) for l in range(seq)))
+
+
+def test_qkv_split_inverse_and_autograd():
+    g = np.random.default_rng(32)
+    batch, seq, heads, d = 3, 5, 4, 8
+    H = heads * d
+    qkv = f16(g.normal(size=(batch * seq, 3 * H)))
+    out = oracle.bias_qkv_split(qkv, np.zeros(3 * H, np.float16), batch, seq, heads)
+    np.testing.assert_array_equal(oracle.bias_qkv_split_bwd(out, batch, seq, heads)[0], qkv)
+    bias = f16(g.normal(size=3 * H))
+    xt = torch.tensor(qkv.astype(np.float64), requires_grad=True)
+    bt = torch.tensor(bias.astype(np.float64), requires_grad=True)
+    y = (xt + bt).view(batch, seq, 3, heads, d).permute(2, 0, 3, 1, 4)
+    dout = f16(g.normal(size=(3, batch, heads, seq, d)))
+    y.backward(torch.tensor(dout.astype(np.float64)))
+    dq, db = oracle.bias_qkv_split_bwd(dout, batch, seq, heads)
+    np.testing.assert_array_equal(dq, xt.grad.numpy().astype(np.float16))
+    np.testing.assert_array_equal(db, bt.grad.numpy().astype(np.float16))
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
 
