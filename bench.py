@@ -356,6 +356,21 @@ def extra_rows(torch, ops):
     del sets, acc, zf, ids, P
     torch.cuda.empty_cache()
 
+    # Cross-entropy criterion, C4: logits [8192, 32768] (537 MB per set)
+    T4, V4 = synth.C4.tokens, synth.C4.vocab
+    x4 = d(synth.criterion_logits(0, T4))
+    y4 = d(synth.criterion_targets())
+    eps, gs = synth.CRITERION_SMOOTHING, synth.CRITERION_LOSS_SCALE / T4
+    sets = [(x4 if i == 0 else x4.clone(), torch.empty(T4, device="cuda"), torch.empty(T4, device="cuda"),
+             torch.empty_like(x4)) for i in range(2)]
+    fw = [lambda s=s: ops.cross_entropy_fwd(s[0], y4, eps, -1, loss=s[1], lse=s[2]) for s in sets]
+    bw = [lambda s=s: ops.cross_entropy_bwd(s[0], y4, s[2], eps, -1, gs, dlogits=s[3]) for s in sets]
+    shape = f"logits [{T4},{V4}], targets Zipf(1.1), smoothing {eps}"
+    out["cross_entropy_fwd"] = row(shape, cold(fw), 2 * T4 * V4 + 4 * T4 + 8 * T4)
+    out["cross_entropy_bwd"] = row(shape, cold(bw), 4 * T4 * V4 + 4 * T4 + 4 * T4)
+    del sets, fw, bw, x4, y4
+    torch.cuda.empty_cache()
+
     # Adam, 350M parameters (7.7 GB per step: larger than every cache by itself)
     n = synth.C5_PARAMS
     gen.manual_seed(5)

@@ -150,6 +150,29 @@ int ls_bias_qkv_split_bwd(void* dqkv, void* dbias, const void* dout, int64_t bat
                           int64_t heads, int64_t head_dim, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Cross-entropy criterion with label smoothing over vocabulary rows ([L10]
+ * technique 1, slide 12 lists it among the fused reduce kernels; [LS2]
+ * sec. 2.1.3 defers its details to the slides).  Per row t of logits x
+ * (fp16 [rows, vocab]) with target y_t (int32 [rows]) and smoothing eps:
+ *     lse[t]  = log sum_j exp(x[t,j])                               (fp32)
+ *     loss[t] = lse[t] - (1-eps)*x[t,y_t] - eps*mean_j x[t,j]       (fp32)
+ *     dlogits[t,j] = grad_scale * (exp(x[t,j] - lse[t])
+ *                                  - (1-eps)*[j == y_t] - eps/vocab) (fp16)
+ * eps = 0 is the plain negative log-likelihood.  A row whose target equals
+ * ignore_index has loss 0 and a zero gradient; any other target outside
+ * [0, vocab) gives a NaN loss and NaN gradients for its row.  NaN or +inf
+ * logits give NaN.  The forward reads each row once (one-pass running max
+ * and sum, [CS336] sec. 6.2), reduces in a fixed order, and saves lse for
+ * the backward, which takes the forward's lse.  dlogits may alias logits.
+ * eps in [0, 1]; grad_scale finite; rows, vocab < 2^31.
+ * Errors: LS_ERR_SHAPE, LS_ERR_PARAM, LS_ERR_NULL. */
+int ls_cross_entropy_fwd(float* loss, float* lse, const void* logits, const int32_t* targets,
+                         int64_t rows, int64_t vocab, float smoothing, int32_t ignore_index,
+                         void* stream);
+int ls_cross_entropy_bwd(void* dlogits, const void* logits, const int32_t* targets, const float* lse,
+                         int64_t rows, int64_t vocab, float smoothing, int32_t ignore_index,
+                         float grad_scale, void* stream);
+
 /* LayerNorm forward with one fused reduction pass ([L10] technique 2,
  * slide 21): per row, S1 = sum x and S2 = sum x^2 are reduced together;
  * mean = S1/H, var = max(S2/H - mean^2, 0), rstd = 1/sqrt(var + eps),

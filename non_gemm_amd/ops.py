@@ -147,6 +147,38 @@ def bias_qkv_split_bwd(dout, dqkv=None, dbias=None, workspace=None):
     return dqkv, dbias
 
 
+def cross_entropy_fwd(logits, targets, smoothing=0.0, ignore_index=-1, loss=None, lse=None):
+    """logits [rows, vocab] fp16, targets int32 [rows] -> (loss fp32 [rows], lse fp32 [rows])."""
+    _dev(logits, targets, loss, lse)
+    _dtype(logits, _F16, "logits")
+    _dtype(targets, torch.int32, "targets")
+    rows, vocab = _rows_cols(logits)
+    if targets.numel() != rows:
+        raise ValueError("one target per row")
+    loss = torch.empty(rows, dtype=_F32, device=logits.device) if loss is None else loss
+    lse = torch.empty(rows, dtype=_F32, device=logits.device) if lse is None else lse
+    check("ls_cross_entropy_fwd", load().ls_cross_entropy_fwd(
+        _ptr(loss), _ptr(lse), _ptr(logits), _ptr(targets), rows, vocab, float(smoothing), int(ignore_index),
+        _stream()))
+    return loss, lse
+
+
+def cross_entropy_bwd(logits, targets, lse, smoothing=0.0, ignore_index=-1, grad_scale=1.0, dlogits=None):
+    """Gradient of sum_t grad_scale * loss[t] with respect to the logits (fp16, logits' shape)."""
+    _dev(logits, targets, lse, dlogits)
+    _dtype(logits, _F16, "logits")
+    _dtype(targets, torch.int32, "targets")
+    _dtype(lse, _F32, "lse")
+    rows, vocab = _rows_cols(logits)
+    if targets.numel() != rows or lse.numel() != rows:
+        raise ValueError("one target and one lse per row")
+    dlogits = torch.empty_like(logits) if dlogits is None else dlogits
+    check("ls_cross_entropy_bwd", load().ls_cross_entropy_bwd(
+        _ptr(dlogits), _ptr(logits), _ptr(targets), _ptr(lse), rows, vocab, float(smoothing), int(ignore_index),
+        float(grad_scale), _stream()))
+    return dlogits
+
+
 def layernorm_fwd(x, gamma, beta, eps, y=None, mean=None, rstd=None):
     """Returns (y fp16, mean fp32 [rows], rstd fp32 [rows])."""
     _dev(x, gamma, beta, y, mean, rstd)

@@ -41,6 +41,8 @@ from .ops import (  # noqa: F401
     bias_qkv_split_bwd,
     bias_relu_dropout,
     bias_relu_dropout_bwd,
+    cross_entropy_bwd,
+    cross_entropy_fwd,
     dropout_keep,
     dropout_scale,
     embedding_bwd,

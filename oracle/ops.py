@@ -182,6 +182,65 @@ def bias_qkv_split_bwd(dout, batch, seq_len, heads):
 
 
 # ----------------------------------------------------------------------------
+# Cross-entropy criterion ([L10] technique 1, slide 12; [LS2] sec. 2.1.3)
+# ----------------------------------------------------------------------------
+
+
+def _xent_rows(logits, targets, smoothing, ignore_index):
+    x = np.asarray(logits, dtype=np.float64)
+    y = np.asarray(targets, dtype=np.int64).reshape(-1)
+    eps = float(np.float32(smoothing))
+    if not 0.0 <= eps <= 1.0:
+        raise ValueError("smoothing must lie in [0, 1]")
+    m = x.max(axis=1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        lse = m + np.log(np.exp(x - m[:, None]).sum(axis=1))       # two passes: max, then sum
+    ignored = y == ignore_index
+    bad = ~ignored & ((y < 0) | (y >= x.shape[1]))
+    return x, y, eps, lse, ignored, bad
+
+
+def cross_entropy_fwd(logits, targets, smoothing, ignore_index):
+    """Label-smoothed cross entropy per row.
+
+    lse = log sum_j exp(x_j); loss = lse - (1 - eps) x_y - eps mean_j x_j,
+    i.e. (1 - eps) (-log p_y) + eps mean_j (-log p_j).  The pages name the
+    criterion and defer its details; label smoothing eps is a parameter
+    (eps = 0: plain cross entropy).  A row whose target equals ignore_index
+    has loss 0; any other target outside [0, V) gives NaN.
+    logits fp16 [rows, V]; targets int [rows].
+    Returns (loss fp32 [rows], lse fp32 [rows]).
+    Parity: pinned by tests (torch.nn.functional.cross_entropy with
+    label_smoothing and ignore_index in float64; scipy logsumexp).
+    """
+    x, y, eps, lse, ignored, bad = _xent_rows(logits, targets, smoothing, ignore_index)
+    loss = np.zeros(x.shape[0])
+    ok = ~ignored & ~bad
+    rows = np.nonzero(ok)[0]
+    loss[rows] = lse[rows] - (1.0 - eps) * x[rows, y[rows]] - eps * x[rows].mean(axis=1)
+    loss[bad] = np.nan
+    return loss.astype(np.float32), lse.astype(np.float32)
+
+
+def cross_entropy_bwd(logits, targets, smoothing, ignore_index, grad_scale):
+    """Gradient of sum_t grad_scale * loss_t with respect to the logits:
+    grad_scale (softmax(x) - (1 - eps) onehot(y) - eps / V), zero on ignored
+    rows, NaN on rows with an out-of-range target; rounded once to fp16.
+    Parity: pinned by tests (torch autograd of cross_entropy in float64).
+    """
+    x, y, eps, lse, ignored, bad = _xent_rows(logits, targets, smoothing, ignore_index)
+    v = x.shape[1]
+    with np.errstate(invalid="ignore", over="ignore"):
+        g = np.exp(x - lse[:, None]) - eps / v
+    ok = ~ignored & ~bad
+    rows = np.nonzero(ok)[0]
+    g[rows, y[rows]] -= 1.0 - eps
+    g[ignored] = 0.0
+    g[bad] = np.nan
+    return (float(np.float32(grad_scale)) * g).astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm ([L10] technique 2, slides 21-22)
 # ----------------------------------------------------------------------------
 

@@ -154,6 +154,31 @@ def embedding_inputs(shape=C4, config=4, zipf_s=1.1):
     }
 
 
+CRITERION_ROW_CHUNK = 256
+CRITERION_SMOOTHING = 0.1     # label smoothing of the Transformer-big translation setting
+CRITERION_LOSS_SCALE = 4096.0  # fp16 loss scale: mean-over-tokens gradients stay representable
+
+
+def criterion_targets(shape=C4, config=4, zipf_s=1.1):
+    """Next-token targets for the C4 criterion: the same Zipf(1.1) law as the ids."""
+    return zipf_ids(rng(config, stream=2), (shape.tokens,), shape.vocab, zipf_s)
+
+
+def criterion_logits(r0, r1, shape=C4, config=4):
+    """Rows [r0, r1) of the C4 logits [tokens, vocab], N(0, 1) in fp16.
+
+    Rows come in chunks of CRITERION_ROW_CHUNK drawn from independent streams,
+    so any row range can be regenerated on its own.
+    """
+    out = np.empty((r1 - r0, shape.vocab), np.float16)
+    c0, c1 = r0 // CRITERION_ROW_CHUNK, (r1 - 1) // CRITERION_ROW_CHUNK
+    for c in range(c0, c1 + 1):
+        block = normal16(rng(config, stream=1000 + c), (CRITERION_ROW_CHUNK, shape.vocab), 1.0)
+        lo, hi = max(r0, c * CRITERION_ROW_CHUNK), min(r1, (c + 1) * CRITERION_ROW_CHUNK)
+        out[lo - r0:hi - r0] = block[lo - c * CRITERION_ROW_CHUNK:hi - c * CRITERION_ROW_CHUNK]
+    return out
+
+
 def adam_chunk(chunk, n=C5_CHUNK, config=5):
     """One chunk of the C5 workspace: p ~ N(0, 0.02), g ~ N(0, 1e-3).
 

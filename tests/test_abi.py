@@ -163,3 +163,16 @@ def test_qkv_split_validation(lib):
     assert lib.ls_bias_qkv_split_bwd(FAKE, None, FAKE, 32, 128, 12, 64, FAKE, need, s) == LS_ERR_NULL
     assert lib.ls_bias_qkv_split_bwd(FAKE, FAKE, None, 32, 128, 12, 64, FAKE, need, s) == LS_ERR_NULL
     assert lib.ls_bias_qkv_split_bwd(None, None, None, 32, 128, 0, 64, None, 0, s) == LS_OK
+
+
+def test_cross_entropy_validation(lib):
+    s = None
+    assert lib.ls_cross_entropy_fwd(FAKE, FAKE, FAKE, FAKE, -1, 100, 0.1, -1, s) == LS_ERR_SHAPE
+    assert lib.ls_cross_entropy_fwd(FAKE, FAKE, FAKE, FAKE, 4, 100, 1.5, -1, s) == LS_ERR_PARAM
+    assert lib.ls_cross_entropy_fwd(FAKE, FAKE, FAKE, FAKE, 4, 100, float("nan"), -1, s) == LS_ERR_PARAM
+    assert lib.ls_cross_entropy_fwd(FAKE, None, FAKE, FAKE, 4, 100, 0.1, -1, s) == LS_ERR_NULL
+    assert lib.ls_cross_entropy_fwd(FAKE, FAKE, FAKE, FAKE, 4, 0, 0.1, -1, s) == LS_ERR_SHAPE
+    assert lib.ls_cross_entropy_fwd(None, None, None, None, 0, 100, 0.1, -1, s) == LS_OK
+    assert lib.ls_cross_entropy_bwd(FAKE, FAKE, FAKE, None, 4, 100, 0.1, -1, 1.0, s) == LS_ERR_NULL
+    assert lib.ls_cross_entropy_bwd(FAKE, FAKE, FAKE, FAKE, 4, 100, 0.1, -1, float("inf"), s) == LS_ERR_PARAM
+    assert lib.ls_cross_entropy_bwd(None, None, None, None, 0, 100, 0.1, -1, 1.0, s) == LS_OK

@@ -256,6 +256,67 @@ def test_bias_qkv_split_dispatch_and_empty(ls):
 
 
 # ----------------------------------------------------------------------------
+# Cross-entropy criterion
+# ----------------------------------------------------------------------------
+
+def assert_xent_rows(loss, lse, dx, x, y, eps, ignore, g, what):
+    ref_loss, ref_lse = oracle.cross_entropy_fwd(x, y, eps, ignore)
+    assert_fp32(lse, ref_lse, what + " lse", floor=1.0)
+    assert_fp32(loss, ref_loss, what + " loss", floor=1.0)
+    assert_fp16(dx, oracle.cross_entropy_bwd(x, y, eps, ignore, g), what + " dlogits")
+
+
+def test_cross_entropy_c4_sampled_rows(ls):
+    """Transformer-big criterion: logits [8192, 32768], Zipf targets, eps 0.1;
+    every row computed on the GPU, the oracle on 64 sampled rows."""
+    T, V = synth.C4.tokens, synth.C4.vocab
+    x = synth.criterion_logits(0, T)
+    y = synth.criterion_targets()
+    xd, yd = dev(x), dev(y)
+    loss, lse = ls.cross_entropy_fwd(xd, yd, synth.CRITERION_SMOOTHING, -1)
+    assert last_dispatch() == "cross_entropy_fwd/row_block512_v8"
+    gs = synth.CRITERION_LOSS_SCALE / T           # mean over tokens, times the loss scale
+    dx = ls.cross_entropy_bwd(xd, yd, lse, synth.CRITERION_SMOOTHING, -1, gs)
+    assert last_dispatch() == "cross_entropy_bwd/vec8"
+    rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(7).integers(0, T, 61)]))
+    assert_xent_rows(host(loss)[rows], host(lse)[rows], host(dx)[rows], x[rows], y[rows],
+                     synth.CRITERION_SMOOTHING, -1, gs, "cross_entropy C4")
+
+
+@pytest.mark.parametrize("rows,v", [(37, 1001), (5, 8), (1, 1), (3, 50257), (64, 4096), (17, 16392), (9, 2048)])
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+def test_cross_entropy_shapes(ls, rows, v, eps):
+    g = np.random.default_rng(rows * 131 + v)
+    x = synth.normal16(g, (rows, v), 2.0)
+    y = g.integers(0, v, size=rows).astype(np.int32)
+    if rows > 2:
+        y[1] = -100                              # ignored
+    xd = dev(x)
+    loss, lse = ls.cross_entropy_fwd(xd, dev(y), eps, -100)
+    what = f"cross_entropy {rows}x{v} eps={eps} [{last_dispatch()}]"
+    dx = ls.cross_entropy_bwd(xd, dev(y), lse, eps, -100, 0.5)
+    assert_xent_rows(host(loss), host(lse), host(dx), x, y, eps, -100, 0.5, what)
+
+
+def test_cross_entropy_nan_bad_target_alias(ls):
+    g = np.random.default_rng(9)
+    x = synth.normal16(g, (6, 1024), 1.0)
+    x[2, 17] = np.nan
+    x[3, 5] = np.inf
+    y = np.array([3, 1024, 7, 8, -1, 0], np.int32)          # row 1: out of range; row 4: ignored
+    xd = dev(x)
+    loss, lse = ls.cross_entropy_fwd(xd, dev(y), 0.1, -1)
+    lo = host(loss)
+    assert np.isnan(lo[[1, 2, 3]]).all() and lo[4] == 0 and np.isfinite(lo[[0, 5]]).all()
+    ref_loss, _ = oracle.cross_entropy_fwd(x, y, 0.1, -1)
+    assert np.isnan(ref_loss[[1, 2, 3]]).all()
+    dx = ls.cross_entropy_bwd(xd, dev(y), lse, 0.1, -1, 1.0, dlogits=xd)      # in place
+    d = host(dx)
+    assert np.isnan(d[1]).all() and (d[4] == 0).all()
+    assert_fp16(d[[0, 5]], oracle.cross_entropy_bwd(x[[0, 5]], y[[0, 5]], 0.1, -1, 1.0), "in-place dlogits")
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
 

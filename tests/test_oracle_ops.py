@@ -206,6 +206,51 @@ def test_qkv_split_inverse_and_autograd():
 
 
 # ----------------------------------------------------------------------------
+# Cross-entropy criterion
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("eps", [0.0, 0.1, 1.0])
+def test_xent_matches_torch_and_logsumexp(eps):
+    g = np.random.default_rng(41)
+    rows, v, ignore = 23, 57, 3
+    x = f16(g.normal(0, 3, size=(rows, v)))
+    y = g.integers(0, v, size=rows).astype(np.int32)
+    y[[2, 7]] = ignore
+    loss, lse = oracle.cross_entropy_fwd(x, y, eps, ignore)
+    x64 = torch.tensor(x.astype(np.float64), requires_grad=True)
+    ref = torch.nn.functional.cross_entropy(x64, torch.tensor(y.astype(np.int64)), reduction="none",
+                                            label_smoothing=eps, ignore_index=ignore)
+    np.testing.assert_array_equal(loss, ref.detach().numpy().astype(np.float32))
+    np.testing.assert_array_equal(lse, scipy.special.logsumexp(x.astype(np.float64), axis=1).astype(np.float32))
+    assert loss[2] == 0 and loss[7] == 0
+    (0.75 * ref).sum().backward()
+    dx = oracle.cross_entropy_bwd(x, y, eps, ignore, 0.75)
+    np.testing.assert_array_equal(dx, x64.grad.numpy().astype(np.float16))
+    assert (dx[[2, 7]] == 0).all()
+
+
+def test_xent_invariants_and_bad_targets():
+    """Each gradient row sums to 0 (softmax and the smoothed one-hot both sum
+    to 1); a uniform row has loss log V; a target outside [0, V) gives NaN."""
+    g = np.random.default_rng(42)
+    x = f16(g.normal(size=(9, 40)))
+    y = g.integers(0, 40, size=9).astype(np.int32)
+    y[4] = 40
+    y[5] = -7
+    loss, _ = oracle.cross_entropy_fwd(x, y, 0.1, -1)
+    assert np.isnan(loss[4]) and np.isnan(loss[5]) and np.isfinite(np.delete(loss, [4, 5])).all()
+    dx = oracle.cross_entropy_bwd(x, y, 0.1, -1, 1.0)
+    assert np.isnan(dx[4]).all() and np.isnan(dx[5]).all()
+    x64 = x.astype(np.float64)
+    lse = scipy.special.logsumexp(x64, axis=1, keepdims=True)
+    full = np.exp(x64 - lse) - 0.1 / 40
+    full[np.arange(9), np.clip(y, 0, 39)] -= 0.9
+    np.testing.assert_allclose(np.delete(full, [4, 5], axis=0).sum(1), 0, atol=1e-12)
+    u, _ = oracle.cross_entropy_fwd(np.zeros((2, 1000), np.float16), np.array([0, 999], np.int32), 0.3, -1)
+    np.testing.assert_allclose(u, np.log(1000), rtol=1e-7)
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
 
