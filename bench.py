@@ -371,6 +371,20 @@ def extra_rows(torch, ops):
     del sets, fw, bw, x4, y4
     torch.cuda.empty_cache()
 
+    # HARS beam top-k, one Transformer-big decoder step: 128 sentences x beam 4 x vocab 32768
+    nb_, nk_ = 128, 4
+    sets = []
+    for _ in range(16):
+        lg = torch.randn((nb_, nk_, V4), device="cuda", generator=gen)
+        sets.append((torch.log_softmax(lg, dim=-1), torch.randn((nb_, nk_), device="cuda", generator=gen),
+                     torch.empty((nb_, nk_), device="cuda"), torch.empty((nb_, nk_), dtype=torch.int32, device="cuda")))
+        del lg
+    calls = [lambda s=s: ops.beam_topk(s[0], nk_, s[1], top_scores=s[2], top_ids=s[3]) for s in sets]
+    out["beam_topk"] = row(f"log-probs [{nb_},{nk_},{V4}] fp32 + beam scores, k {nk_}", cold(calls),
+                           4 * nb_ * nk_ * V4 + 4 * nb_ * nk_ + 8 * nb_ * nk_)
+    del sets, calls
+    torch.cuda.empty_cache()
+
     # Adam, 350M parameters (7.7 GB per step: larger than every cache by itself)
     n = synth.C5_PARAMS
     gen.manual_seed(5)

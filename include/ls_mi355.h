@@ -173,6 +173,33 @@ int ls_cross_entropy_bwd(void* dlogits, const void* logits, const int32_t* targe
                          int64_t rows, int64_t vocab, float smoothing, int32_t ignore_index,
                          float grad_scale, void* stream);
 
+/* Beam-search top-k by hierarchical filtering (HARS, the inference part of
+ * [L10], beam search slides 45-54).  For each batch element b the
+ * candidates are
+ *     c[i, v] = log_probs[b, i, v] + beam_scores[b, i]     (one fp32 add)
+ * over beams i < beam and vocabulary entries v < vocab; the call returns
+ * the k largest, in descending order, ties broken by the smaller flat index
+ * i * vocab + v: top_scores fp32 [batch, k] and top_ids int32 [batch, k]
+ * (flat indices).  Ordering is total: every NaN ranks above +inf and -0
+ * below +0; a NaN score is returned as the default quiet NaN.  beam_scores
+ * may be NULL: then c = log_probs exactly.
+ * Steps, per beam: its candidates split into k groups, the smallest group
+ * maximum bounds the beam's k-th best from below, only candidates at or
+ * above it are kept and sorted, and the beam's best k go to the workspace;
+ * then the beam x k winners of each batch element are sorted.  Heavily tied
+ * rows (more than 4096 survivors) fall back to k exact selection passes,
+ * with the same result.
+ * log_probs: fp32 [batch, beam, vocab].  1 <= k <= min(1024, beam*vocab),
+ * beam * k <= 4096, beam * vocab < 2^31.  workspace: device memory of
+ * ls_beam_topk_workspace_bytes(batch, beam, k) bytes, 8-byte aligned, no
+ * initialisation, not shared with a concurrent call.
+ * Errors: LS_ERR_SHAPE, LS_ERR_UNSUPPORTED (k > 1024 or beam * k > 4096),
+ * LS_ERR_NULL, LS_ERR_WORKSPACE, LS_ERR_PARAM (misaligned workspace). */
+size_t ls_beam_topk_workspace_bytes(int64_t batch, int64_t beam, int64_t k);
+int ls_beam_topk(float* top_scores, int32_t* top_ids, const float* log_probs, const float* beam_scores,
+                 int64_t batch, int64_t beam, int64_t vocab, int64_t k, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* LayerNorm forward with one fused reduction pass ([L10] technique 2,
  * slide 21): per row, S1 = sum x and S2 = sum x^2 are reduced together;
  * mean = S1/H, var = max(S2/H - mean^2, 0), rstd = 1/sqrt(var + eps),

@@ -38,6 +38,9 @@ SIGNATURES = {
                                      ctypes.c_int32, c_void_p]),
     "ls_cross_entropy_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_f32,
                                      ctypes.c_int32, c_f32, c_void_p]),
+    "ls_beam_topk_workspace_bytes": (c_size, [c_i64, c_i64, c_i64]),
+    "ls_beam_topk": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p,
+                             c_size, c_void_p]),
     "ls_layernorm_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_i64, c_i64, c_f32, c_void_p]),
     "ls_layernorm_bwd_workspace_bytes": (c_size, [c_i64, c_i64]),

@@ -179,6 +179,30 @@ def cross_entropy_bwd(logits, targets, lse, smoothing=0.0, ignore_index=-1, grad
     return dlogits
 
 
+def beam_topk(log_probs, k, beam_scores=None, top_scores=None, top_ids=None, workspace=None):
+    """log_probs fp32 [batch, beam, vocab] (+ beam_scores fp32 [batch, beam]) ->
+    (top_scores fp32 [batch, k], top_ids int32 [batch, k], flat i * vocab + v)."""
+    _dev(log_probs, beam_scores, top_scores, top_ids, workspace)
+    _dtype(log_probs, _F32, "log_probs")
+    if log_probs.dim() != 3:
+        raise ValueError("log_probs must be [batch, beam, vocab]")
+    batch, beam, vocab = log_probs.shape
+    if beam_scores is not None:
+        _dtype(beam_scores, _F32, "beam_scores")
+        if beam_scores.shape != (batch, beam):
+            raise ValueError("beam_scores must be [batch, beam]")
+    top_scores = torch.empty((batch, k), dtype=_F32, device=log_probs.device) if top_scores is None else top_scores
+    top_ids = torch.empty((batch, k), dtype=torch.int32, device=log_probs.device) if top_ids is None else top_ids
+    lib = load()
+    if workspace is None:
+        need = int(lib.ls_beam_topk_workspace_bytes(batch, beam, int(k)))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=log_probs.device)
+    check("ls_beam_topk", lib.ls_beam_topk(
+        _ptr(top_scores), _ptr(top_ids), _ptr(log_probs), _ptr(beam_scores), batch, beam, vocab, int(k),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return top_scores, top_ids
+
+
 def layernorm_fwd(x, gamma, beta, eps, y=None, mean=None, rstd=None):
     """Returns (y fp16, mean fp32 [rows], rstd fp32 [rows])."""
     _dev(x, gamma, beta, y, mean, rstd)

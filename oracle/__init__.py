@@ -45,7 +45,9 @@ from .ops import (  # noqa: F401
     cross_entropy_fwd,
     dropout_keep,
     dropout_scale,
+    beam_candidates,
     embedding_bwd,
+    hars_topk,
     embedding_fwd,
     layernorm_bwd,
     layernorm_fwd,

@@ -241,6 +241,72 @@ def cross_entropy_bwd(logits, targets, smoothing, ignore_index, grad_scale):
 
 
 # ----------------------------------------------------------------------------
+# Beam-search top-k by hierarchical filtering (HARS; [L10] beam search slides)
+# ----------------------------------------------------------------------------
+
+
+def _rank_keys(c):
+    """Unsigned keys monotone in the float32 value: -0 < +0, every NaN largest."""
+    u = np.asarray(c, np.float32).view(np.uint32).astype(np.uint64)
+    key = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
+    return np.where(np.isnan(c), np.uint64(0xFFFFFFFF), key).astype(np.uint64)
+
+
+def beam_candidates(log_probs, beam_scores):
+    """c[b, i, v] = log_probs[b, i, v] + beam_scores[b, i], one float32 add."""
+    lp = np.asarray(log_probs, np.float32)
+    if beam_scores is None:
+        return lp.copy()
+    return (lp + np.asarray(beam_scores, np.float32)[:, :, None]).astype(np.float32)
+
+
+def hars_topk(log_probs, beam_scores, k, return_survivors=False):
+    """Top-k of each batch element's beam x V candidates, by the pages' steps.
+
+    1. split every beam's V candidates into k groups (contiguous, as even as
+       possible) and take each group's maximum;
+    2. the smallest of the k maxima, R_i, is reached by at least k of the
+       beam's candidates; R = max over beams of R_i (the pages leave the
+       combination across beams open: any beam's R_i bounds the k-th best
+       candidate from below, the largest is the tightest);
+    3. keep the candidates >= R (the pages say "greater than"; a group
+       maximum equal to R can itself be among the best k, so equality must be
+       kept) and sort them: value descending, ties by the smaller flat index
+       i * V + v.
+    A beam with fewer than k candidates gives no bound.
+    log_probs float32 [batch, beam, V]; beam_scores float32 [batch, beam] or
+    None.  Returns (scores float32 [batch, k], flat ids int32 [batch, k]) and,
+    with return_survivors, the survivor count per batch element.
+    Parity: pinned by tests (a full sort of every candidate gives the same
+    top-k; the bound holds; a beam 2, vocab 8 case keeps 5 of 16).
+    """
+    c = beam_candidates(log_probs, beam_scores)
+    batch, beam, v = c.shape
+    if not 1 <= k <= beam * v:
+        raise ValueError("need 1 <= k <= beam * V")
+    keys = _rank_keys(c)
+    scores = np.empty((batch, k), np.float32)
+    ids = np.empty((batch, k), np.int32)
+    survivors = np.empty(batch, np.int64)
+    for b in range(batch):
+        r = np.uint64(0)
+        for i in range(beam):
+            if v >= k:
+                maxima = [g.max() for g in np.array_split(keys[b, i], k)]
+                r = max(r, min(maxima))
+        flat = keys[b].reshape(-1)
+        kept = np.nonzero(flat >= r)[0]
+        survivors[b] = kept.size
+        order = np.lexsort((kept, -flat[kept].astype(np.int64)))      # key descending, index ascending
+        best = kept[order[:k]]
+        ids[b] = best
+        scores[b] = c[b].reshape(-1)[best]
+    if return_survivors:
+        return scores, ids, survivors
+    return scores, ids
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm ([L10] technique 2, slides 21-22)
 # ----------------------------------------------------------------------------
 

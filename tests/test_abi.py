@@ -176,3 +176,21 @@ def test_cross_entropy_validation(lib):
     assert lib.ls_cross_entropy_bwd(FAKE, FAKE, FAKE, None, 4, 100, 0.1, -1, 1.0, s) == LS_ERR_NULL
     assert lib.ls_cross_entropy_bwd(FAKE, FAKE, FAKE, FAKE, 4, 100, 0.1, -1, float("inf"), s) == LS_ERR_PARAM
     assert lib.ls_cross_entropy_bwd(None, None, None, None, 0, 100, 0.1, -1, 1.0, s) == LS_OK
+
+
+def test_beam_topk_validation(lib):
+    s = None
+    need = lib.ls_beam_topk_workspace_bytes(2, 4, 4)
+    assert need == 2 * 4 * 4 * 8
+    assert lib.ls_beam_topk_workspace_bytes(2, 64, 128) == 0
+    w = (FAKE, need)
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, -1, 4, 100, 4, *w, s) == LS_ERR_SHAPE
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 4, 100, 401, *w, s) == LS_ERR_SHAPE
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 4, 1000, 1025, *w, s) == LS_ERR_UNSUPPORTED
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 8, 1000, 1000, *w, s) == LS_ERR_UNSUPPORTED
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 1 << 16, 1 << 16, 4, *w, s) == LS_ERR_SHAPE
+    assert lib.ls_beam_topk(FAKE, None, FAKE, None, 2, 4, 100, 4, *w, s) == LS_ERR_NULL
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 4, 100, 4, FAKE, need - 8, s) == LS_ERR_WORKSPACE
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 4, 100, 4, None, need, s) == LS_ERR_NULL
+    assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 4, 100, 4, ctypes.c_void_p(0x1004), need, s) == LS_ERR_PARAM
+    assert lib.ls_beam_topk(None, None, None, None, 0, 4, 100, 4, None, 0, s) == LS_OK

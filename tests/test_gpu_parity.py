@@ -317,6 +317,53 @@ def test_cross_entropy_nan_bad_target_alias(ls):
 
 
 # ----------------------------------------------------------------------------
+# HARS beam-search top-k (indices and scores bit-exact)
+# ----------------------------------------------------------------------------
+
+def check_topk(ls, lp, bs, k, what):
+    s, i = ls.beam_topk(dev(lp), k, None if bs is None else dev(bs))
+    ref_s, ref_i = oracle.hars_topk(lp, bs, k)
+    got_i, got_s = host(i), host(s)
+    assert np.array_equal(got_i, ref_i), f"{what}: ids {got_i[:2]} vs oracle {ref_i[:2]}"
+    nan = np.isnan(ref_s)
+    assert np.array_equal(np.isnan(got_s), nan), what                 # NaN payloads are not kept
+    assert np.array_equal(got_s[~nan].view(np.uint32), ref_s[~nan].view(np.uint32)), what
+
+
+def test_beam_topk_decoder_step(ls):
+    """Transformer-big decoder step: 128 sentences x beam 4 over vocab 32768."""
+    g = np.random.default_rng(17)
+    logits = g.normal(size=(128, 4, 32768))
+    lp = (logits - np.log(np.exp(logits).sum(-1, keepdims=True))).astype(np.float32)
+    bs = np.cumsum(g.normal(-1.0, 0.5, size=(128, 4)), axis=1).astype(np.float32)
+    check_topk(ls, lp, bs, 4, "beam_topk 128x4x32768")
+    assert last_dispatch() == "beam_topk/hars_rows_block1024_merge"
+
+
+@pytest.mark.parametrize("batch,beam,v,k", [(3, 2, 8, 2), (5, 1, 1, 1), (2, 3, 100003, 7), (4, 8, 50257, 8),
+                                            (2, 4, 1000, 64), (3, 2, 600, 1000), (1, 16, 4096, 16),
+                                            (2, 5, 33, 5), (7, 3, 32768, 3)])
+def test_beam_topk_shapes(ls, batch, beam, v, k):
+    g = np.random.default_rng(batch * 7 + beam * 13 + v + k)
+    lp = g.normal(size=(batch, beam, v)).astype(np.float32)
+    bs = g.normal(size=(batch, beam)).astype(np.float32) if beam > 1 else None
+    check_topk(ls, lp, bs, k, f"beam_topk {batch}x{beam}x{v} k={k}")
+
+
+def test_beam_topk_ties_special_values_and_overflow(ls):
+    lp = np.zeros((2, 3, 40), np.float32)
+    lp[0, 0, 1] = -0.0
+    lp[0, 1, 4] = np.nan
+    lp[0, 2, 5] = np.inf
+    lp[1, :, ::7] = 3.0
+    check_topk(ls, lp, None, 6, "ties and special values")
+    # every candidate equal: all 131072 survive the threshold, more than the
+    # survivor list holds, so the exact-pass fallback answers
+    check_topk(ls, np.zeros((2, 4, 32768), np.float32), None, 4, "all equal")
+    check_topk(ls, np.full((1, 2, 5000), -1.5, np.float32), np.zeros((1, 2), np.float32), 3, "all equal, small")
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
 

@@ -251,6 +251,66 @@ def test_xent_invariants_and_bad_targets():
 
 
 # ----------------------------------------------------------------------------
+# HARS beam-search top-k
+# ----------------------------------------------------------------------------
+
+def _full_sort_topk(lp, bs, k):
+    """Every candidate sorted: value descending (NaN first, -0 below +0), then index."""
+    c = oracle.beam_candidates(lp, bs)
+    batch = c.shape[0]
+    flat = c.reshape(batch, -1)
+    out_s, out_i = [], []
+    for b in range(batch):
+        vals = flat[b].astype(np.float64)
+        nan = np.isnan(vals)
+        neg0 = (vals == 0) & np.signbit(vals)
+        order = sorted(range(vals.size), key=lambda j: (0 if nan[j] else 1, -vals[j] if not nan[j] else 0,
+                                                       1 if neg0[j] else 0, j))
+        best = np.array(order[:k])
+        out_i.append(best)
+        out_s.append(flat[b][best])
+    return np.array(out_s, np.float32), np.array(out_i, np.int32)
+
+
+@pytest.mark.parametrize("batch,beam,v,k", [(3, 4, 50, 4), (2, 1, 9, 9), (2, 3, 2, 4), (1, 5, 40, 1)])
+def test_hars_equals_full_sort(batch, beam, v, k):
+    g = np.random.default_rng(batch * 100 + v)
+    lp = g.normal(size=(batch, beam, v)).astype(np.float32)
+    bs = g.normal(size=(batch, beam)).astype(np.float32)
+    if v > 3:
+        lp[0, 0, :3] = lp[0, 0, 3]            # ties: the smaller index ranks first
+    s, i, surv = oracle.hars_topk(lp, bs, k, return_survivors=True)
+    s2, i2 = _full_sort_topk(lp, bs, k)
+    np.testing.assert_array_equal(i, i2)
+    np.testing.assert_array_equal(s.view(np.uint32), s2.view(np.uint32))
+    assert (surv >= k).all() and (surv <= beam * v).all()
+
+
+def test_hars_special_values_and_ties():
+    lp = np.zeros((1, 2, 6), np.float32)
+    lp[0, 0, 1] = -0.0
+    lp[0, 1, 4] = np.nan
+    lp[0, 1, 5] = np.inf
+    s, i = oracle.hars_topk(lp, None, 4)
+    s2, i2 = _full_sort_topk(lp, None, 4)
+    np.testing.assert_array_equal(i, i2)
+    assert i[0, 0] == 10 and i[0, 1] == 11            # NaN first, then +inf
+    assert list(i[0, 2:]) == [0, 2]                   # +0 ties by index; the -0 at 1 ranks below them
+    s, i = oracle.hars_topk(np.ones((1, 3, 4), np.float32), None, 5)
+    assert list(i[0]) == [0, 1, 2, 3, 4]
+
+
+def test_hars_worked_example_keeps_5_of_16():
+    """Beam 2, vocabulary 8, k = 2: 16 candidates, 5 of them at or above the
+    threshold (groups of 4: beam 0 maxima 10 and 8.75, beam 1 maxima 9.5 and
+    8.5, so R = max(8.75, 8.5))."""
+    lp = np.array([[[10, 1, 9, 2, 3, 8.75, 4, 7], [9.5, 9.25, 0, 0, 8.5, 0, 0, 0]]], np.float32)
+    s, i, surv = oracle.hars_topk(lp, None, 2, return_survivors=True)
+    assert lp.size == 16 and surv[0] == 5
+    assert list(i[0]) == [0, 8] and list(s[0]) == [10.0, 9.5]
+
+
+# ----------------------------------------------------------------------------
 # LayerNorm
 # ----------------------------------------------------------------------------
 
