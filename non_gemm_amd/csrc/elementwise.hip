@@ -14,47 +14,47 @@ namespace ls {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr unsigned kGridCap = 8192;
 
-template <bool RESID, bool RELU, bool DROP, int VPT>
+template <bool RESID, bool RELU, bool DROP>
+__device__ __forceinline__ void elementwise_vec8(half8* out, const half8 xv, const half8 bv, const half8 rv,
+                                                 uint32_t v, const Dropout& d) {
+    float a[8], b[8], r[8], f[8], o[8];
+    unpack8(xv, a);
+    unpack8(bv, b);
+    if (RESID) unpack8(rv, r);
+    if (DROP) {
+        dropout_factors8(d, v, f);   // the vector index is the Philox call index
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = 1.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        float t = a[k] + b[k];
+        if (RELU) t = t < 0.0f ? 0.0f : t;   // NaN propagates
+        o[k] = RESID ? fmaf(f[k], t, r[k]) : t * f[k];
+    }
+    __builtin_nontemporal_store(pack8(o), out + v);
+}
+
+// One 16-byte vector per lane per iteration; the grid holds at most
+// kGridCap blocks (four full-occupancy generations on 256 CUs), so larger
+// tensors loop.  The loads of an iteration are issued before its Philox
+// rounds, which run while they are in flight.
+template <bool RESID, bool RELU, bool DROP>
 __global__ __launch_bounds__(kBlock) void elementwise_vec_kernel(
     half8* out, const half8* x, const half8* bias, const half8* res, uint32_t nvec,
     FastDiv col_vecs, Dropout d) {
-    const uint32_t base = blockIdx.x * (kBlock * VPT) + threadIdx.x;
-    half8 xv[VPT], bv[VPT], rv[VPT];
-    // Issue every load of this thread before any arithmetic.
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const uint32_t v = base + j * kBlock;
-        if (v < nvec) {
-            // Streamed operands: non-temporal loads and stores keep them from
-            // displacing reusable lines (the bias) in the caches.
-            xv[j] = __builtin_nontemporal_load(x + v);
-            if (RESID) rv[j] = __builtin_nontemporal_load(res + v);
-            bv[j] = bias[col_vecs.mod(v)];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const uint32_t v = base + j * kBlock;
-        if (v < nvec) {
-            float a[8], b[8], r[8], f[8], o[8];
-            unpack8(xv[j], a);
-            unpack8(bv[j], b);
-            if (RESID) unpack8(rv[j], r);
-            if (DROP) {
-                dropout_factors8(d, v, f);   // the vector index is the Philox call index
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) f[k] = 1.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float t = a[k] + b[k];
-                if (RELU) t = t < 0.0f ? 0.0f : t;   // NaN propagates
-                o[k] = RESID ? fmaf(f[k], t, r[k]) : t * f[k];
-            }
-            __builtin_nontemporal_store(pack8(o), out + v);
-        }
+    const uint32_t stride = gridDim.x * kBlock;
+    for (uint32_t v = blockIdx.x * kBlock + threadIdx.x; v < nvec; v += stride) {
+        // Streamed operands: non-temporal loads and stores keep them from
+        // displacing reusable lines (the bias) in the caches.
+        const half8 bv = bias[col_vecs.mod(v)];
+        const half8 xv = __builtin_nontemporal_load(x + v);
+        half8 rv{};
+        if (RESID) rv = __builtin_nontemporal_load(res + v);
+        elementwise_vec8<RESID, RELU, DROP>(out, xv, bv, rv, v, d);
     }
 }
 
@@ -117,20 +117,19 @@ int launch_elementwise(const char* name, void* out, const void* x, const void* b
                      (!RESID || aligned16(res)) && (n / 8) < (1ull << 31) &&
                      static_cast<uint64_t>(cols / 8) < (1ull << 31);
     if (vec) {
-        constexpr int VPT = 1;
         const uint32_t nvec = static_cast<uint32_t>(n / 8);
         const FastDiv cv(static_cast<uint32_t>(cols / 8));
-        const unsigned grid = grid_for(nvec, kBlock * VPT, 1u << 30);
+        const unsigned grid = grid_for(nvec, kBlock, kGridCap);
         auto* o = static_cast<half8*>(out);
         auto* xv = static_cast<const half8*>(x);
         auto* bv = static_cast<const half8*>(bias);
         auto* rv = static_cast<const half8*>(res);
         if (drop)
-            elementwise_vec_kernel<RESID, RELU, true, VPT><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
+            elementwise_vec_kernel<RESID, RELU, true><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
         else
-            elementwise_vec_kernel<RESID, RELU, false, VPT><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
-        set_dispatch(drop ? (RESID ? "bias_dropout_residual/vec8_vpt1" : "bias_relu_dropout/vec8_vpt1")
-                          : (RESID ? "bias_dropout_residual/vec8_vpt1_p0" : "bias_relu_dropout/vec8_vpt1_p0"));
+            elementwise_vec_kernel<RESID, RELU, false><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
+        set_dispatch(drop ? (RESID ? "bias_dropout_residual/vec8" : "bias_relu_dropout/vec8")
+                          : (RESID ? "bias_dropout_residual/vec8_p0" : "bias_relu_dropout/vec8_p0"));
     } else {
         const unsigned grid = grid_for(n, kBlock, 65536);
         auto* o = static_cast<half_t*>(out);
