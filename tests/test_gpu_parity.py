@@ -702,3 +702,62 @@ def test_probe_copy_and_read(ls, nbytes):
     scale = np.abs(pad).reshape(nsink, 256).sum(axis=1)
     assert np.all(np.abs(got[:nsink] - want) <= 1e-5 * scale + 1e-30)
     assert np.all(got[nsink:] == -7.0)        # nothing written past ceil(bytes / 1024)
+
+
+# ----------------------------------------------------------------------------
+# HIP graph replay: the chain's launches captured once and replayed, with
+# eager work and synchronisation between replays; every replay must equal the
+# eager result bit for bit (no memset nodes, no state carried between calls)
+# ----------------------------------------------------------------------------
+
+def test_graph_replay_matches_eager(ls):
+    g = np.random.default_rng(77)
+    T, H, F = 256, 768, 3072
+    x = dev(synth.normal16(g, (T, H), 1.0))
+    r = dev(synth.normal16(g, (T, H), 1.0))
+    b = dev(synth.normal16(g, (H,), 0.02))
+    gm = dev(synth.uniform16(g, (H,), 0.5, 1.5))
+    bt = dev(synth.normal16(g, (H,), 0.1))
+    f = dev(synth.normal16(g, (T, F), 1.0))
+    fb = dev(synth.normal16(g, (F,), 0.02))
+    dy = dev(synth.normal16(g, (T, H), 1.0))
+    sc = dev(synth.normal16(g, (2, 12, 128, 128), 1.0))
+    out = {k: torch.empty_like(v) for k, v in (("z", x), ("y", x), ("a", f), ("dx", x), ("s", sc), ("ds", sc))}
+    mean, rstd = torch.empty(T, device="cuda"), torch.empty(T, device="cuda")
+    dg, db = torch.empty(H, dtype=torch.float16, device="cuda"), torch.empty(H, dtype=torch.float16, device="cuda")
+    ws = torch.empty(ls.layernorm_bwd_workspace_bytes(T, H), dtype=torch.uint8, device="cuda")
+    ids = dev(g.integers(0, 500, size=(2, 128)).astype(np.int32))
+    dE = torch.empty((500, H), dtype=torch.float32, device="cuda")
+    edy = dev(synth.normal16(g, (256, H), 1.0))
+
+    def step():
+        ls.bias_dropout_residual(x, b, r, 0.1, SEED, 0, out=out["z"])
+        ls.layernorm_fwd(out["z"], gm, bt, 1e-5, y=out["y"], mean=mean, rstd=rstd)
+        ls.bias_relu_dropout(f, fb, 0.1, SEED, 1, out=out["a"])
+        ls.layernorm_bwd(dy, out["z"], gm, mean, rstd, dx=out["dx"], dgamma=dg, dbeta=db, workspace=ws)
+        ls.softmax_fwd(sc, y=out["s"])
+        ls.softmax_bwd(out["s"], sc, dx=out["ds"])
+        ls.embedding_bwd(ids, edy, dE, 16.0, 0.1, SEED, 3, zero_first=True)
+
+    def snap():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (*out.values(), mean, rstd, dg, db, dE)]
+
+    step()
+    ref = snap()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    for rep in range(3):
+        for t in (*out.values(), mean, rstd, dg, db, dE):
+            t.fill_(7)                         # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snap()
+        for i, (a, e) in enumerate(zip(got[:-1], ref[:-1])):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.float16 else a.view(torch.int32),
+                               e.view(torch.int16) if e.dtype == torch.float16 else e.view(torch.int32)), \
+                f"replay {rep}: output {i} differs from the eager run"
+        # the embedding gradient adds with atomics in no fixed order: equal up to fp32 rounding
+        assert torch.allclose(got[-1], ref[-1], rtol=1e-5, atol=1e-4), f"replay {rep}: embedding gradient"
