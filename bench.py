@@ -12,10 +12,10 @@ Inputs are synthetic (seeded, shaped like the layer) and resident in HBM before
 the timed region.  R independent buffer sets (> 2 GB in total) are rotated so
 that no step finds its tensors in the 256 MB Infinity Cache.  Each set's step is
 captured as one HIP graph.  Every 8th timed step is replayed split around the
-largest kernel (bias+ReLU+dropout), which is then launched directly between two
-HIP events on the same stream (created without the system-scope fence, so they
-bracket the kernel alone): the events sample that kernel's duration live inside
-the timed region (the roofline line).
+largest kernel (bias+ReLU+dropout), which is then launched directly on the same
+stream with a pair of HIP events attached to the launch (hipExtLaunchKernel
+records them when the kernel starts and ends): the events sample that kernel's
+duration live inside the timed region (the roofline line).
 
 Output: one JSON line.  `value` is algorithmic chain bytes per second (the
 fused-minimum bytes: every input read once, every output written once, the
@@ -79,8 +79,9 @@ def source_hash():
 
 
 # ---------------------------------------------------------------------------
-# HIP events without the system-scope release fence: recorded around one
-# kernel they time the kernel itself (a default event's fence adds ~2 us).
+# HIP events for the dominant kernel, handed to the library with
+# ls_time_next_launch(): its launch records them itself (hipExtLaunchKernel),
+# so each pair brackets that kernel's execution and nothing else.
 # ---------------------------------------------------------------------------
 
 class KernelEvents:
@@ -103,8 +104,10 @@ class KernelEvents:
                     raise RuntimeError("hipEventCreateWithFlags failed")
             self.pairs.append((a, b))
 
-    def record(self, i, which, stream):
-        self.hip.hipEventRecord(self.pairs[i][which], self.ct.c_void_p(stream))
+    def arm(self, i, lib):
+        """The next elementwise launch of this thread records pair i."""
+        if lib.ls_time_next_launch(self.pairs[i][0], self.pairs[i][1]) != 0:
+            raise RuntimeError("ls_time_next_launch failed")
 
     def mean_us(self):
         tot = 0.0
@@ -616,10 +619,8 @@ def main():
         else:
             g_a.replay()
         if sampled:
-            ev.record(i // SAMPLE, 0, S)
+            ev.arm(i // SAMPLE, lib)
         fn(*a)
-        if sampled:
-            ev.record(i // SAMPLE, 1, S)
         if args.eager:
             for nm, _, f, aa in s.launches[dom_idx + 1:]:
                 f(*aa)

@@ -58,6 +58,7 @@ SIGNATURES = {
     "ls_dropout_mask": (c_int, [c_void_p, c_i64, c_f32, c_u64, c_u64, c_void_p]),
     "ls_probe_copy": (c_int, [c_void_p, c_void_p, c_i64, c_void_p]),
     "ls_probe_read": (c_int, [c_void_p, c_void_p, c_i64, c_void_p]),
+    "ls_time_next_launch": (c_int, [c_void_p, c_void_p]),
     "ls_dropout_decision_bits": (c_int, []),
     "ls_status_string": (ctypes.c_char_p, [c_int]),
     "ls_last_error": (ctypes.c_char_p, []),

@@ -9,6 +9,8 @@
 namespace {
 thread_local char g_last_error[512] = "";
 thread_local char g_last_dispatch[128] = "";
+thread_local hipEvent_t g_time_start = nullptr;   // events for the next timed launch
+thread_local hipEvent_t g_time_stop = nullptr;
 }  // namespace
 
 namespace ls {
@@ -26,6 +28,14 @@ void set_dispatch(const char* name) {
 }
 
 void clear_hip_error() { (void)hipGetLastError(); }
+
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_time_start) return false;
+    *start = g_time_start;
+    *stop = g_time_stop;
+    g_time_start = g_time_stop = nullptr;
+    return true;
+}
 
 int launch_status(const char* what) {
     const hipError_t e = hipGetLastError();
@@ -51,6 +61,16 @@ const char* ls_status_string(int status) {
         case LS_ERR_UNIMPLEMENTED: return "not implemented";
         default: return "unknown status";
     }
+}
+
+int ls_time_next_launch(void* start_event, void* stop_event) {
+    if (!start_event || !stop_event) {
+        g_time_start = g_time_stop = nullptr;
+        return ls::fail(LS_ERR_NULL, "ls_time_next_launch: null event");
+    }
+    g_time_start = static_cast<hipEvent_t>(start_event);
+    g_time_stop = static_cast<hipEvent_t>(stop_event);
+    return LS_OK;
 }
 
 const char* ls_last_error(void) { return g_last_error; }

@@ -125,9 +125,9 @@ int launch_elementwise(const char* name, void* out, const void* x, const void* b
         auto* bv = static_cast<const half8*>(bias);
         auto* rv = static_cast<const half8*>(res);
         if (drop)
-            elementwise_vec_kernel<RESID, RELU, true><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
+            launch_kernel(elementwise_vec_kernel<RESID, RELU, true>, grid, kBlock, 0, s, o, xv, bv, rv, nvec, cv, d);
         else
-            elementwise_vec_kernel<RESID, RELU, false><<<grid, kBlock, 0, s>>>(o, xv, bv, rv, nvec, cv, d);
+            launch_kernel(elementwise_vec_kernel<RESID, RELU, false>, grid, kBlock, 0, s, o, xv, bv, rv, nvec, cv, d);
         set_dispatch(drop ? (RESID ? "bias_dropout_residual/vec8" : "bias_relu_dropout/vec8")
                           : (RESID ? "bias_dropout_residual/vec8_p0" : "bias_relu_dropout/vec8_p0"));
     } else {
@@ -137,9 +137,9 @@ int launch_elementwise(const char* name, void* out, const void* x, const void* b
         auto* bs = static_cast<const half_t*>(bias);
         auto* rs = static_cast<const half_t*>(res);
         if (drop)
-            elementwise_scalar_kernel<RESID, RELU, true><<<grid, kBlock, 0, s>>>(o, xs, bs, rs, n, cols, d);
+            launch_kernel(elementwise_scalar_kernel<RESID, RELU, true>, grid, kBlock, 0, s, o, xs, bs, rs, n, cols, d);
         else
-            elementwise_scalar_kernel<RESID, RELU, false><<<grid, kBlock, 0, s>>>(o, xs, bs, rs, n, cols, d);
+            launch_kernel(elementwise_scalar_kernel<RESID, RELU, false>, grid, kBlock, 0, s, o, xs, bs, rs, n, cols, d);
         set_dispatch(RESID ? "bias_dropout_residual/scalar" : "bias_relu_dropout/scalar");
     }
     return launch_status(name);

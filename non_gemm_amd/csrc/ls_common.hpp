@@ -6,6 +6,7 @@
 // thread-local error / dispatch bookkeeping of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +32,25 @@ int fail(int status, const char* fmt, ...);       // records ls_last_error, retu
 void set_dispatch(const char* name);
 int launch_status(const char* what);              // LS_OK or LS_ERR_HIP after a launch
 void clear_hip_error();
+
+// Events armed by ls_time_next_launch() for the calling thread, consumed by
+// the next launch that goes through launch_kernel().
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Launches kernel<<<grid, block, lds, stream>>>(args...); if the calling
+// thread armed a pair of timing events, the launch records them itself
+// (hipExtLaunchKernel), so they bracket the kernel's execution and nothing
+// else.
+template <typename... KArgs, typename... Args>
+void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                   Args... args) {
+    hipEvent_t start, stop;
+    if (take_launch_events(&start, &stop))
+        hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), stream, start, stop, 0u,
+                              static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, lds, stream>>>(static_cast<KArgs>(args)...);
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool host_finite(float x) { return std::isfinite(x); }

@@ -194,3 +194,9 @@ def test_beam_topk_validation(lib):
     assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 4, 100, 4, None, need, s) == LS_ERR_NULL
     assert lib.ls_beam_topk(FAKE, FAKE, FAKE, None, 2, 4, 100, 4, ctypes.c_void_p(0x1004), need, s) == LS_ERR_PARAM
     assert lib.ls_beam_topk(None, None, None, None, 0, 4, 100, 4, None, 0, s) == LS_OK
+
+
+def test_time_next_launch_validation(lib):
+    assert lib.ls_time_next_launch(None, FAKE) == LS_ERR_NULL
+    assert lib.ls_time_next_launch(FAKE, None) == LS_ERR_NULL
+    assert b"null event" in lib.ls_last_error()

@@ -761,3 +761,26 @@ def test_graph_replay_matches_eager(ls):
                 f"replay {rep}: output {i} differs from the eager run"
         # the embedding gradient adds with atomics in no fixed order: equal up to fp32 rounding
         assert torch.allclose(got[-1], ref[-1], rtol=1e-5, atol=1e-4), f"replay {rep}: embedding gradient"
+
+
+def test_timed_launch_same_result_and_events(ls):
+    """ls_time_next_launch: the armed launch gives the same output, its events
+    measure a positive duration, and the next call runs untimed."""
+    from non_gemm_amd import _lib
+    lib = _lib.load()
+    g = np.random.default_rng(12)
+    x = dev(synth.normal16(g, (4096, 3072), 1.0))
+    b = dev(synth.normal16(g, (3072,), 0.02))
+    ref = host(ls.bias_relu_dropout(x, b, 0.1, SEED, 1))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()                  # torch creates its events on first use
+    torch.cuda.synchronize()
+    assert lib.ls_time_next_launch(e0.cuda_event, e1.cuda_event) == 0
+    out = ls.bias_relu_dropout(x, b, 0.1, SEED, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint16), ref.view(np.uint16))
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 10.0
+    out2 = ls.bias_relu_dropout(x, b, 0.1, SEED, 1)        # disarmed: plain launch
+    assert np.array_equal(host(out2).view(np.uint16), ref.view(np.uint16))
