@@ -137,7 +137,12 @@ struct Raw;
 template <>
 struct Raw<8> {
     using T = half8;
+    // dy and x are read once: non-temporal loads stream them past the caches.
     static __device__ __forceinline__ T load(const half_t* p, size_t i) {
+        return __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + i));
+    }
+    // gamma is read by every block: a plain load keeps it cached.
+    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) {
         return *reinterpret_cast<const half8*>(p + i);
     }
     static __device__ __forceinline__ T zero() { return half8{0, 0, 0, 0, 0, 0, 0, 0}; }
@@ -147,6 +152,7 @@ template <>
 struct Raw<1> {
     using T = half_t;
     static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) { return p[i]; }
     static __device__ __forceinline__ T zero() { return static_cast<half_t>(0.0f); }
     static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
 };
@@ -181,7 +187,7 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const uint32_t c = (l + j * LPR) * CW;
-        gr[j] = c < h ? R::load(gamma, c) : R::zero();
+        gr[j] = c < h ? R::load_reused(gamma, c) : R::zero();
 #pragma unroll
         for (int k = 0; k < CW; ++k) acc_g[j][k] = acc_b[j][k] = 0.0f;
     }
