@@ -51,6 +51,35 @@ struct Chunk<1> {
     }
 };
 
+// Raw 16-byte (or 2-byte) row chunks.  A conditional load goes into a
+// register set that was zeroed beforehand, so no instruction writes those
+// registers after the load and every load of a row stays in flight until the
+// first arithmetic that needs it.
+template <int CW>
+struct Raw;
+template <>
+struct Raw<8> {
+    using T = half8;
+    // Row data (x, dy) are read once: non-temporal loads stream them past the caches.
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) {
+        return __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + i));
+    }
+    // gamma and beta are read by every block: a plain load keeps them cached.
+    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) {
+        return *reinterpret_cast<const half8*>(p + i);
+    }
+    static __device__ __forceinline__ T zero() { return half8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    static __device__ __forceinline__ void widen(const T& r, float f[8]) { unpack8(r, f); }
+};
+template <>
+struct Raw<1> {
+    using T = half_t;
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ T zero() { return static_cast<half_t>(0.0f); }
+    static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
+};
+
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
@@ -65,34 +94,33 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
     const int l = lane % LPR;
     const int sub = lane / LPR;
 
-    float g[NCH][CW], b[NCH][CW];
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        const uint32_t c = (l + j * LPR) * CW;
-        if (c < h) {
-            Chunk<CW>::load(gamma, c, g[j]);
-            Chunk<CW>::load(beta, c, b[j]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < CW; ++k) g[j][k] = b[j][k] = 0.0f;
-        }
-    }
+    using R = Raw<CW>;
     const float hf = static_cast<float>(h);
     for (uint32_t r0 = blockIdx.x * (kWaves * RPW); r0 < rows; r0 += gridDim.x * (kWaves * RPW)) {
         const uint32_t row = r0 + wave * RPW + sub;
         const bool ok = row < rows;
         const size_t base = static_cast<size_t>(row) * h;
-        float v[NCH][CW];
+        // The row's chunks first, then gamma and beta (cache hits after the
+        // first waves); one wait covers all of them.
+        typename R::T xr[NCH], gr[NCH], br[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) xr[j] = gr[j] = br[j] = R::zero();
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            if (ok && c < h) xr[j] = R::load(x, base + c);
+        }
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
             if (ok && c < h) {
-                Chunk<CW>::load(x, base + c, v[j]);
-            } else {
-#pragma unroll
-                for (int k = 0; k < CW; ++k) v[j][k] = 0.0f;
+                gr[j] = R::load_reused(gamma, c);
+                br[j] = R::load_reused(beta, c);
             }
         }
+        float v[NCH][CW];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) R::widen(xr[j], v[j]);
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
@@ -115,8 +143,11 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
             const uint32_t c = (l + j * LPR) * CW;
             if (ok && c < h) {
                 float o[CW];
+                float g[CW], b[CW];
+                R::widen(gr[j], g);
+                R::widen(br[j], b);
 #pragma unroll
-                for (int k = 0; k < CW; ++k) o[k] = fmaf((v[j][k] - mu) * rs, g[j][k], b[j][k]);
+                for (int k = 0; k < CW; ++k) o[k] = fmaf((v[j][k] - mu) * rs, g[k], b[k]);
                 Chunk<CW>::store(y, base + c, o);
             }
         }
@@ -132,31 +163,6 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
 // accumulators are folded: first across the row groups inside each wave
 // (shuffles), then across waves through one LDS slot per wave, and the block
 // writes its partial row [2h] = (dgamma part, dbeta part).
-template <int CW>
-struct Raw;
-template <>
-struct Raw<8> {
-    using T = half8;
-    // dy and x are read once: non-temporal loads stream them past the caches.
-    static __device__ __forceinline__ T load(const half_t* p, size_t i) {
-        return __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + i));
-    }
-    // gamma is read by every block: a plain load keeps it cached.
-    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) {
-        return *reinterpret_cast<const half8*>(p + i);
-    }
-    static __device__ __forceinline__ T zero() { return half8{0, 0, 0, 0, 0, 0, 0, 0}; }
-    static __device__ __forceinline__ void widen(const T& r, float f[8]) { unpack8(r, f); }
-};
-template <>
-struct Raw<1> {
-    using T = half_t;
-    static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
-    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) { return p[i]; }
-    static __device__ __forceinline__ T zero() { return static_cast<half_t>(0.0f); }
-    static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
-};
-
 // Up to 16 waves per block when a lane holds <= 16 elements, else 8 (register
 // budget); the wave slots of the column fold take at most 128 KiB of LDS.
 template <int NCH, int CW>
