@@ -209,14 +209,13 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
         const bool ok = row < rows;
         const size_t base = static_cast<size_t>(row) * h;
 #pragma unroll
+        for (int j = 0; j < NCH; ++j) ody[j] = ox[j] = R::zero();
+#pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
             if (ok && c < h) {
                 ody[j] = R::load(dy, base + c);
                 ox[j] = R::load(x, base + c);
-            } else {
-                ody[j] = R::zero();
-                ox[j] = R::zero();
             }
         }
         omu = ok ? mean[row] : 0.0f;
