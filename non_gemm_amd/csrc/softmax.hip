@@ -28,20 +28,30 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int CW>
 struct Chunk;
 // Score rows are streamed once: non-temporal 16-byte loads and stores.
+// Loads go into raw registers filled beforehand (fill(), then a conditional
+// load()), so nothing writes them after the load and all loads of a row are
+// in flight before the first wait; widen() converts once they are needed.
 template <>
 struct Chunk<8> {
-    static __device__ __forceinline__ void load(const half_t* p, size_t i, float f[8]) {
-        unpack8(__builtin_nontemporal_load(reinterpret_cast<const half8*>(p + i)), f);
+    using T = half8;
+    static __device__ __forceinline__ T fill(float v) {
+        const half_t h = static_cast<half_t>(v);
+        return half8{h, h, h, h, h, h, h, h};
     }
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) {
+        return __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + i));
+    }
+    static __device__ __forceinline__ void widen(const T& r, float f[8]) { unpack8(r, f); }
     static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[8]) {
         __builtin_nontemporal_store(pack8(f), reinterpret_cast<half8*>(p + i));
     }
 };
 template <>
 struct Chunk<1> {
-    static __device__ __forceinline__ void load(const half_t* p, size_t i, float f[1]) {
-        f[0] = static_cast<float>(p[i]);
-    }
+    using T = half_t;
+    static __device__ __forceinline__ T fill(float v) { return static_cast<half_t>(v); }
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
     static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[1]) {
         p[i] = static_cast<half_t>(f[0]);
     }
@@ -87,17 +97,17 @@ __global__ __launch_bounds__(kBlock) void softmax_fwd_kernel(half_t* y, const ha
         const bool ok = row < rows;
         const uint32_t n = ok ? valid_keys<MASKED>(mask, row, k) : 0u;
         const size_t base = static_cast<size_t>(row) * k;
-        float v[NCH][CW];
+        typename Chunk<CW>::T raw[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) raw[j] = Chunk<CW>::fill(-INFINITY);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
-            if (c < n) {
-                Chunk<CW>::load(x, base + c, v[j]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < CW; ++q) v[j][q] = -INFINITY;
-            }
+            if (c < n) raw[j] = Chunk<CW>::load(x, base + c);
         }
+        float v[NCH][CW];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) Chunk<CW>::widen(raw[j], v[j]);
         float m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
@@ -144,17 +154,22 @@ __global__ __launch_bounds__(kBlock) void softmax_bwd_kernel(half_t* dx, const h
         const uint32_t row = r0 + wave * RPW + sub;
         const bool ok = row < rows;
         const size_t base = static_cast<size_t>(row) * k;
-        float vy[NCH][CW], vd[NCH][CW];
+        typename Chunk<CW>::T ry[NCH], rd[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) ry[j] = rd[j] = Chunk<CW>::fill(0.0f);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
             if (ok && c < k) {
-                Chunk<CW>::load(y, base + c, vy[j]);
-                Chunk<CW>::load(dy, base + c, vd[j]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < CW; ++q) vy[j][q] = vd[j][q] = 0.0f;
+                ry[j] = Chunk<CW>::load(y, base + c);
+                rd[j] = Chunk<CW>::load(dy, base + c);
             }
+        }
+        float vy[NCH][CW], vd[NCH][CW];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            Chunk<CW>::widen(ry[j], vy[j]);
+            Chunk<CW>::widen(rd[j], vd[j]);
         }
         float dot = 0.0f;
 #pragma unroll
@@ -213,17 +228,20 @@ __global__ __launch_bounds__(kBigBlock) void softmax_fwd_block_kernel(half_t* y,
     for (uint32_t row = blockIdx.x; row < rows; row += gridDim.x) {
         const uint32_t n = valid_keys<MASKED>(mask, row, k);
         const size_t base = static_cast<size_t>(row) * k;
+        half8 raw[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) raw[j] = Chunk<8>::fill(-INFINITY);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (threadIdx.x + j * kBigBlock) * 8;
+            if (c < n) raw[j] = Chunk<8>::load(x, base + c);
+        }
         float v[NCH][8];
         float m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (threadIdx.x + j * kBigBlock) * 8;
-            if (c < n) {
-                Chunk<8>::load(x, base + c, v[j]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) v[j][q] = -INFINITY;
-            }
+            Chunk<8>::widen(raw[j], v[j]);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 if (MASKED && c + q >= n) v[j][q] = -INFINITY;
@@ -262,18 +280,23 @@ __global__ __launch_bounds__(kBigBlock) void softmax_bwd_block_kernel(half_t* dx
     __shared__ float red[kBigWaves];
     for (uint32_t row = blockIdx.x; row < rows; row += gridDim.x) {
         const size_t base = static_cast<size_t>(row) * k;
-        float vy[NCH][8], vd[NCH][8];
-        float dot = 0.0f;
+        half8 ry[NCH], rd[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) ry[j] = rd[j] = Chunk<8>::fill(0.0f);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (threadIdx.x + j * kBigBlock) * 8;
             if (c < k) {
-                Chunk<8>::load(y, base + c, vy[j]);
-                Chunk<8>::load(dy, base + c, vd[j]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) vy[j][q] = vd[j][q] = 0.0f;
+                ry[j] = Chunk<8>::load(y, base + c);
+                rd[j] = Chunk<8>::load(dy, base + c);
             }
+        }
+        float vy[NCH][8], vd[NCH][8];
+        float dot = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            Chunk<8>::widen(ry[j], vy[j]);
+            Chunk<8>::widen(rd[j], vd[j]);
 #pragma unroll
             for (int q = 0; q < 8; ++q) dot = fmaf(vy[j][q], vd[j][q], dot);
         }
