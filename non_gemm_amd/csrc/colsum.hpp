@@ -20,7 +20,7 @@ constexpr int kCsBlock = kCsWaves * kWave;      // 1024 threads
 constexpr int kSegVecs = kWave;                 // 64 vectors = 512 columns per segment
 constexpr int kSegCols = kSegVecs * 8;
 constexpr int kMaxGroups = 256;
-constexpr int kTargetWaves = 6144;              // ~24 waves per CU keep enough loads in flight
+constexpr int kTargetWaves = 8192;              // two 16-wave blocks per CU: full occupancy
 
 // Row groups: as many as keep ~kTargetWaves waves busy, at most one per 16
 // rows (every wave gets a row) and at most kMaxGroups.  A function of the

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kBlock) void emb_fwd_vec_kernel(half_t* out, const 
 #pragma unroll
                     for (int k = 0; k < 8; ++k) o[k] = __builtin_nanf("");
                 }
-                orow[cv] = pack8(o);
+                __builtin_nontemporal_store(pack8(o), orow + cv);   // written once: stream it
             }
         }
     }
