@@ -368,7 +368,7 @@ def test_beam_topk_ties_special_values_and_overflow(ls):
 # ----------------------------------------------------------------------------
 
 LN_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (1000, 64), (77, 96), (33, 512), (9, 1536),
-             (5, 2048), (3, 4096), (50, 100), (20, 13), (1, 8), (300, 768)]
+             (5, 2048), (3, 4096), (50, 100), (20, 13), (1, 8), (300, 768), (4, 4095)]
 
 
 def ln_inputs(rows, h, seed):
@@ -462,7 +462,7 @@ def test_softmax_fwd_c2_masked(ls, causal, with_lengths):
     assert np.all(y[~valid] == 0), tag + ": masked entries must be exactly 0"
 
 
-@pytest.mark.parametrize("k", [64, 100, 128, 4096, 8192])
+@pytest.mark.parametrize("k", [64, 100, 128, 4096, 8192, 65536])
 def test_softmax_fwd_edge_lengths(ls, k):
     """Key lengths 0, 1, ragged and beyond k (clamped); causal rows."""
     g = np.random.default_rng(k)
@@ -784,3 +784,16 @@ def test_timed_launch_same_result_and_events(ls):
     assert 0.0 < ms < 10.0
     out2 = ls.bias_relu_dropout(x, b, 0.1, SEED, 1)        # disarmed: plain launch
     assert np.array_equal(host(out2).view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("k", [16384, 65536])
+def test_softmax_longest_rows_fwd_bwd(ls, k):
+    """The block-per-row path up to its largest row (65536 keys)."""
+    g = np.random.default_rng(k + 1)
+    x = synth.normal16(g, (1, 1, 3, k), 3.0)
+    y = ls.softmax_fwd(dev(x))
+    assert_fp16(host(y), oracle.softmax_fwd(x, None, False), f"softmax_fwd k={k} [{last_dispatch()}]")
+    dy = synth.normal16(g, (3, k), 1.0)
+    yr = oracle.softmax_fwd(x, None, False).reshape(3, k)
+    dx = ls.softmax_bwd(dev(yr), dev(dy))
+    assert_fp16(host(dx), oracle.softmax_bwd(yr, dy), f"softmax_bwd k={k} [{last_dispatch()}]")
