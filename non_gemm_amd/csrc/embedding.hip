@@ -118,32 +118,10 @@ constexpr int kSliceCols = kWave * 8;     // columns per wave
 constexpr int kBatch = 16;                // dy rows in flight per lane
 constexpr uint64_t kNoToken = ~0ull;
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
     const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
     return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Ascending bitonic sort of one 64-bit key per lane across the wave.
-__device__ __forceinline__ uint64_t wave_sort(uint64_t key, int lane) {
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t other = shfl_xor_u64(key, j);
-            const bool ascending = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            const uint64_t lo = key < other ? key : other;
-            const uint64_t hi = key < other ? other : key;
-            key = (lower == ascending) ? lo : hi;
-        }
-    }
-    return key;
 }
 
 template <bool DROP>
@@ -170,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void emb_bwd_kernel(float* dE, const int32_
         if (id >= 0 && static_cast<uint32_t>(id) < vocab)
             key = (static_cast<uint64_t>(id) << 8) | static_cast<uint32_t>(lane);
     }
-    key = wave_sort(key, lane);
+    key = wave_sort_asc(key, lane);
     const uint64_t next = __shfl_down(static_cast<unsigned long long>(key), 1);
     const uint64_t ends = __ballot(lane == kWave - 1 || (next >> 8) != (key >> 8));
     const int count = __popcll(__ballot(key != kNoToken));

@@ -176,6 +176,29 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// 64-bit lane exchange, and an ascending bitonic sort of one 64-bit key per
+// lane across the whole wave (lane 0 ends with the smallest key).
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_sort_asc(uint64_t key, int lane) {
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t other = shfl_xor_u64(key, j);
+            const bool ascending = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            const uint64_t lo = key < other ? key : other;
+            const uint64_t hi = key < other ? other : key;
+            key = (lower == ascending) ? lo : hi;
+        }
+    }
+    return key;
+}
+
 // ---------------------------------------------------------------------------
 // Unsigned division by a runtime constant d (1 <= d < 2^31) for numerators
 // n < 2^31: q = (mulhi(n, m) + n) >> s with s = ceil(log2 d) and

@@ -106,27 +106,35 @@ __global__ __launch_bounds__(kTkBlock) void beam_row_topk_kernel(uint64_t* best,
         return c * kChunk + (static_cast<uint32_t>(u) * kTkBlock + tid) * 4 + e;
     };
     // Candidate values of chunk c into x[] (slots past the row end are never
-    // kept: keep() checks the index); returns the lane's largest key.
+    // kept: keep() checks the index); returns the lane's largest key.  With
+    // vocab % 4 == 0 a vector either lies inside the row or wholly past it.
     auto load_chunk = [&](uint32_t c, float x[kChunkVec * 4]) {
-        uint32_t mk = 0;
+        // Every load of the chunk is issued before the first value is used.
+        float4v q[kChunkVec];
 #pragma unroll
-        for (int u = 0; u < kChunkVec; ++u) {
-            const uint32_t e0 = elem(c, u, 0);
-            float4v q = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            if (vec && e0 + 3 < vocab) {
-                q = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(row + e0));
-            } else {
+        for (int u = 0; u < kChunkVec; ++u) q[u] = float4v{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (vec) {
+#pragma unroll
+            for (int u = 0; u < kChunkVec; ++u) {
+                const uint32_t e0 = elem(c, u, 0);
+                if (e0 < vocab) q[u] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(row + e0));
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kChunkVec; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (e0 + e < vocab) q[e] = row[e0 + e];
-            }
+                    if (elem(c, u, e) < vocab) q[u][e] = row[elem(c, u, e)];
+        }
+        uint32_t mk = 0;
+#pragma unroll
+        for (int u = 0; u < kChunkVec; ++u)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float v = q[e] + add;                   // the one fp32 add of the definition
+                const float v = q[u][e] + add;                // the one fp32 add of the definition
                 x[u * 4 + e] = v;
-                if (e0 + e < vocab) mk = max(mk, key_of(v));
+                if (elem(c, u, e) < vocab) mk = max(mk, key_of(v));
             }
-        }
         return mk;
     };
     auto keep = [&](uint32_t c, const float x[kChunkVec * 4], uint32_t thr) {
@@ -191,6 +199,15 @@ __global__ __launch_bounds__(kTkBlock) void beam_row_topk_kernel(uint64_t* best,
     __syncthreads();
     uint64_t* out = best + static_cast<size_t>(rowid) * k;
     const uint32_t count = sh.count;
+    if (count <= static_cast<uint32_t>(kWave) && k <= static_cast<uint32_t>(kWave)) {
+        // Short list: one wave sorts it in registers, no block barriers.
+        if (wave == 0) {
+            uint64_t key = static_cast<uint32_t>(lane) < count ? sh.list[lane] : 0;
+            key = ~wave_sort_asc(~key, lane);          // descending; the padding ranks 0 come last
+            if (static_cast<uint32_t>(lane) < k) out[lane] = key;
+        }
+        return;
+    }
     if (count <= kCap) {
         uint32_t n = 2;
         while (n < count || n < k) n <<= 1;
@@ -231,6 +248,19 @@ __global__ __launch_bounds__(kMergeBlock) void beam_merge_kernel(float* top_scor
     __shared__ uint64_t list[kCap];
     const uint32_t b = blockIdx.x;
     const uint32_t m = beam * k;
+    const uint64_t* src0 = best + static_cast<size_t>(b) * m;
+    if (m <= static_cast<uint32_t>(kWave)) {          // one wave, in registers
+        if (threadIdx.x < kWave) {
+            const int lane = threadIdx.x;
+            uint64_t key = static_cast<uint32_t>(lane) < m ? src0[lane] : 0;
+            key = ~wave_sort_asc(~key, lane);
+            if (static_cast<uint32_t>(lane) < k) {
+                top_scores[static_cast<size_t>(b) * k + lane] = value_of(static_cast<uint32_t>(key >> 32));
+                top_ids[static_cast<size_t>(b) * k + lane] = static_cast<int32_t>(~static_cast<uint32_t>(key));
+            }
+        }
+        return;
+    }
     uint32_t n = 2;
     while (n < m) n <<= 1;
     const uint64_t* src = best + static_cast<size_t>(b) * m;
