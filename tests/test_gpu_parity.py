@@ -86,7 +86,7 @@ def test_dropout_mask_bit_exact(ls, n, p, seed, offset):
 # bias + dropout + residual / bias + ReLU + dropout
 # ----------------------------------------------------------------------------
 
-EW_SHAPES = [(128, 256), (4096, 768), (37, 24), (5, 1000), (3, 13), (1, 8), (0, 64)]
+EW_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (37, 24), (5, 1000), (3, 13), (1, 8), (0, 64)]
 
 
 @pytest.mark.parametrize("rows,cols", EW_SHAPES)
@@ -131,7 +131,8 @@ def test_bias_dropout_residual_aliasing_and_unaligned(ls):
     assert_fp16(out, ref, "unaligned x")
 
 
-@pytest.mark.parametrize("rows,cols", [(4096, 3072), (128, 1024), (37, 24), (5, 1000), (3, 13), (0, 8)])
+@pytest.mark.parametrize("rows,cols", [(4096, 3072), (8192, 4096), (128, 1024), (37, 24), (5, 1000), (3, 13),
+                                       (0, 8)])
 @pytest.mark.parametrize("p", [0.1, 0.0, 1.0])
 def test_bias_relu_dropout(ls, rows, cols, p):
     g = np.random.default_rng(rows * 7 + cols)
@@ -643,6 +644,37 @@ def test_adam_steps(ls, n, decoupled, offset, steps):
     if decoupled or steps == 1:
         assert_fp32(host(mt), rm, tag + " exp_avg")
         assert_fp32(host(vt), rv, tag + " exp_avg_sq")
+
+
+def test_adam_full_workspace_sampled(ls):
+    """The 350M-parameter workspace of the Adam workload, ten single-launch
+    steps on the GPU; the oracle (element-wise) on 200k sampled parameters,
+    chunk boundaries and the last element included."""
+    n = synth.C5_PARAMS
+    nchunks = -(-n // synth.C5_CHUNK)
+    p = np.empty(n, np.float16)
+    gr = np.empty(n, np.float16)
+    for c in range(nchunks):
+        pc, gc = synth.adam_chunk(c)
+        lo, hi = c * synth.C5_CHUNK, min(n, (c + 1) * synth.C5_CHUNK)
+        p[lo:hi], gr[lo:hi] = pc[:hi - lo], gc[:hi - lo]
+    hp = synth.ADAM_HYPER
+    pt, gt = dev(p), dev(gr)
+    mt, vt = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    idx = np.unique(np.concatenate([np.random.default_rng(5).integers(0, n, 200_000),
+                                    np.arange(0, n, synth.C5_CHUNK), [n - 1, n - 8, 7, 8]]))
+    rp, rg = p[idx], gr[idx]
+    rm, rv = np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
+    for step in range(1, synth.ADAM_STEPS + 1):
+        ls.adam_workspace_step(pt, gt, mt, vt, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                               hp["weight_decay"], step, hp["grad_scale"], hp["decoupled_wd"])
+        rp, rm, rv = oracle.adam_workspace_step(rp, rg, rm, rv, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                                hp["weight_decay"], step, hp["grad_scale"], hp["decoupled_wd"])
+    ti = torch.from_numpy(idx).cuda()
+    tag = f"adam 350M sampled [{last_dispatch()}]"
+    assert_fp16(host(pt[ti]), rp, tag + " param")
+    assert_fp32(host(mt[ti]), rm, tag + " exp_avg")
+    assert_fp32(host(vt[ti]), rv, tag + " exp_avg_sq")
 
 
 def test_adam_resume_bit_identical(ls):
