@@ -190,10 +190,10 @@ class ChainSet:
                 check(name, fn(*args))
 
 
-def build_sets(torch, lib, shape, nsets, p, seed, eps):
+def build_sets(torch, lib, shape, nsets, p, seed, eps, config=3):
     import synth
     per, counts, total = chain_bytes(shape.tokens, shape.hidden, shape.ffn, shape.heads, shape.seq)
-    inputs = synth.chain_inputs(shape, config=3)
+    inputs = synth.chain_inputs(shape, config=config)
     sets = [ChainSet(torch, inputs, shape, lib, per, p, seed, eps) for _ in range(nsets)]
     return sets, per, counts, total
 
@@ -475,6 +475,68 @@ def stored_traffic():
 
 # ---------------------------------------------------------------------------
 
+def transformer_big_chain(torch, lib, check, cap_stream, p, seed, eps, nsets=3, reps=20):
+    """The Transformer-big layer (8192 tokens, hidden 1024, 16 heads, FFN 4096)
+    through the same 11 launches plus the embedding forward and backward
+    (vocabulary 32768, Zipf ids, fp32 gradient accumulated), one HIP graph per
+    rotated buffer set (about 0.9 GB each)."""
+    import numpy as np
+
+    import synth
+    shape = synth.C4
+    sets, per, counts, total = build_sets(torch, lib, shape, nsets, p, seed, eps, config=4)
+    inp = synth.embedding_inputs()
+    distinct = int(np.unique(inp["ids"]).size)
+    T, H, V, L = shape.tokens, shape.hidden, shape.vocab, shape.seq
+    emb_f = 4 * T + 2 * H * distinct + 2 * H * L + 2 * T * H
+    emb_b = 4 * T + 2 * T * H + 8 * H * distinct
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    ids, P = d(inp["ids"]), d(inp["pos_emb"])
+    keep = []
+    for s in sets:
+        E, dy = d(inp["tok_emb"]), d(inp["grad_out"])
+        out = torch.empty((T, H), dtype=torch.float16, device="cuda")
+        dE = torch.zeros((V, H), dtype=torch.float32, device="cuda")
+        keep.append((E, dy, out, dE))
+        S = torch.cuda.current_stream().cuda_stream
+        s.launches.append(("embedding_fwd", emb_f, lib.ls_embedding_fwd,
+                           (out.data_ptr(), ids.data_ptr(), E.data_ptr(), P.data_ptr(), shape.batch, L, H, V, L,
+                            inp["scale"], p, seed, synth.SITE_EMBEDDING, S)))
+        s.launches.append(("embedding_bwd", emb_b, lib.ls_embedding_bwd,
+                           (dE.data_ptr(), ids.data_ptr(), dy.data_ptr(), shape.batch, L, H, V, inp["scale"], p, seed,
+                            synth.SITE_EMBEDDING, 0, S)))
+        s.run(check)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            st = torch.cuda.current_stream().cuda_stream
+            for nm, _, fn, a in s.launches:
+                check(nm, fn(*a[:-1], st))
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(graphs))
+    nbytes = total + emb_f + emb_b
+    out = {"shape": "8192 tokens (32 x 256), hidden 1024, 16 heads, FFN 4096, vocab 32768",
+           "calls_per_step": len(sets[0].launches),
+           "kernels_per_step": len(sets[0].launches) + counts["layernorm_bwd"],   # + LayerNorm's column sums
+           "us_per_step": round(us, 2), "bytes_per_step": nbytes,
+           "GB/s": round(nbytes / us / 1e3, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
+           "rotated_sets": nsets}
+    del graphs, sets, keep
+    torch.cuda.empty_cache()
+    return out
+
+
 def attainable(torch, lib, check, cap_stream, dom_bytes):
     """Bandwidth the device reaches with the operators' access pattern: the
     library's reference copy and read kernels over 1 GiB buffers, and a copy
@@ -683,6 +745,7 @@ def main():
     del graphs, sets
     torch.cuda.empty_cache()
     reach = None if args.no_info else attainable(torch, lib, check, cap_stream, per[DOMINANT])
+    big = None if args.no_info else transformer_big_chain(torch, lib, check, cap_stream, p, seed, eps)
 
     extra = None if args.no_extra else extra_rows(torch, ops)
     cpu = None if args.no_cpu else cpu_baseline(shape, p, seed, eps)
@@ -717,6 +780,7 @@ def main():
         "warm_chain_us": None if warm_us is None else round(warm_us, 2),
         "attainable_hbm": reach,
         "dispatch": dispatch,
+        "transformer_big_chain": big,
         "other_rows": extra,
         "wall_s_timed": round(wall, 4),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
