@@ -316,6 +316,51 @@ def extra_rows(torch, ops):
     del calls, fwd_out
     torch.cuda.empty_cache()
 
+    # The chain's kernels at the Transformer-big shapes, each alone on enough
+    # rotated buffer sets (>= 1.2 GB) to miss the Infinity Cache.
+    T4_, H4_, F4_ = synth.C4.tokens, synth.C4.hidden, synth.C4.ffn
+    B4_, NH4_, L4_ = synth.C4.batch, synth.C4.heads, synth.C4.seq
+    per4, _, _ = chain_bytes(T4_, H4_, F4_, NH4_, L4_)
+    sets_for = lambda nbytes: max(4, -(-int(1.2e9) // nbytes))  # noqa: E731
+    emp = lambda *s, dt=torch.float16: torch.empty(s, dtype=dt, device="cuda")  # noqa: E731
+    c4 = {}
+
+    def c4_row(name, calls):
+        us = cold(calls)
+        c4[name] = {"us": round(us, 2), "bytes": per4[name], "GB/s": round(per4[name] / us / 1e3, 1),
+                    "pct_of_peak": round(100 * per4[name] / us / 1e3 / HBM_PEAK_GBPS, 1)}
+
+    R = sets_for(per4["bias_dropout_residual"])
+    bs = [(rnd(T4_, H4_), rnd(H4_), rnd(T4_, H4_), emp(T4_, H4_)) for _ in range(R)]
+    c4_row("bias_dropout_residual", [lambda s=s: ops.bias_dropout_residual(s[0], s[1], s[2], p, seed, 0, out=s[3])
+                                     for s in bs])
+    del bs
+    R = sets_for(per4["bias_relu_dropout"])
+    bs = [(rnd(T4_, F4_), rnd(F4_), emp(T4_, F4_)) for _ in range(R)]
+    c4_row("bias_relu_dropout", [lambda s=s: ops.bias_relu_dropout(s[0], s[1], p, seed, 1, out=s[2]) for s in bs])
+    del bs
+    R = sets_for(per4["layernorm_fwd"])
+    gm, bt = rnd(H4_).abs() + 0.5, rnd(H4_)
+    bs = [(rnd(T4_, H4_), emp(T4_, H4_), emp(T4_, dt=torch.float32), emp(T4_, dt=torch.float32)) for _ in range(R)]
+    c4_row("layernorm_fwd", [lambda s=s: ops.layernorm_fwd(s[0], gm, bt, synth.LN_EPS, y=s[1], mean=s[2], rstd=s[3])
+                             for s in bs])
+    for s in bs:
+        ops.layernorm_fwd(s[0], gm, bt, synth.LN_EPS, y=s[1], mean=s[2], rstd=s[3])
+    R2 = sets_for(per4["layernorm_bwd"])
+    wsn = ops.layernorm_bwd_workspace_bytes(T4_, H4_)
+    bb = [(rnd(T4_, H4_), bs[i % len(bs)], emp(T4_, H4_), emp(H4_), emp(H4_), emp(wsn, dt=torch.uint8))
+          for i in range(R2)]
+    c4_row("layernorm_bwd", [lambda s=s: ops.layernorm_bwd(s[0], s[1][0], gm, s[1][2], s[1][3], dx=s[2], dgamma=s[3],
+                                                           dbeta=s[4], workspace=s[5]) for s in bb])
+    del bs, bb
+    R = sets_for(per4["softmax_bwd"])
+    bs = [(rnd(B4_, NH4_, L4_, L4_), emp(B4_, NH4_, L4_, L4_), rnd(B4_, NH4_, L4_, L4_)) for _ in range(R)]
+    c4_row("softmax_fwd", [lambda s=s: ops.softmax_fwd(s[0], y=s[1]) for s in bs])
+    c4_row("softmax_bwd", [lambda s=s: ops.softmax_bwd(s[1], s[2], dx=s[0]) for s in bs])
+    del bs
+    torch.cuda.empty_cache()
+    out["transformer_big_kernels"] = c4
+
     # Bias + Q/K/V head split and its backward, C3 attention shape
     B, L, NH = synth.C3.batch, synth.C3.seq, synth.C3.heads
     H3 = 3 * H
