@@ -158,16 +158,20 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
 // Backward, row pass
 // ---------------------------------------------------------------------------
 // Blocks of 4..16 waves (sized so that ~one block per CU covers the rows);
-// each wave walks its rows with the next row's loads issued before the
-// current row's reductions.  After the rows, the per-lane column
+// each wave walks its rows, every load of a row issued before the first
+// wait.  (A prefetch of the next row into a second register set measured
+// slower: it costs the registers that a 16-wave block needs.)  After the
+// rows, the per-lane column
 // accumulators are folded: first across the row groups inside each wave
 // (shuffles), then across waves through one LDS slot per wave, and the block
 // writes its partial row [2h] = (dgamma part, dbeta part).
-// Up to 16 waves per block when a lane holds <= 16 elements, else 8 (register
-// budget); the wave slots of the column fold take at most 128 KiB of LDS.
+// Waves per block by register budget: 16 when a lane holds <= 16 elements
+// (<= 128 VGPRs), 8 up to 32 elements, 4 beyond (one wave per SIMD, up to 512
+// VGPRs, so the largest rows do not spill); the wave slots of the column fold
+// take at most 128 KiB of LDS.
 template <int NCH, int CW>
 struct BwdBounds {
-    static constexpr int kMaxThreads = NCH * CW <= 8 ? 1024 : 512;
+    static constexpr int kMaxThreads = NCH * CW <= 16 ? 1024 : (NCH * CW <= 32 ? 512 : 256);
 };
 constexpr size_t kBwdLdsBudget = 128 * 1024;
 
@@ -221,14 +225,9 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
         omu = ok ? mean[row] : 0.0f;
         ors = ok ? rstd[row] : 0.0f;
     };
-    uint32_t r0 = blockIdx.x * per_iter;
-    if (r0 < rows) fetch(r0 + my, rdy, rx, mu, rs);
-    for (; r0 < rows; r0 += stride) {
+    for (uint32_t r0 = blockIdx.x * per_iter; r0 < rows; r0 += stride) {
         const uint32_t row = r0 + my;
-        typename R::T ndy[NCH], nx[NCH];
-        float nmu = 0.0f, nrs = 0.0f;
-        if (r0 + stride < rows) fetch(row + stride, ndy, nx, nmu, nrs);   // prefetch the next row
-
+        fetch(row, rdy, rx, mu, rs);
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
@@ -265,15 +264,6 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
                     Chunk<CW>::store(dx, base + c, o);
                 }
             }
-        }
-        if (r0 + stride < rows) {
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                rdy[j] = ndy[j];
-                rx[j] = nx[j];
-            }
-            mu = nmu;
-            rs = nrs;
         }
     }
 
@@ -409,7 +399,7 @@ struct BwdLaunch {
 BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
     BwdLaunch b;
     const int64_t rpw = kWave / s.lpr;
-    const int max_waves = (s.nch * s.cw <= 8 ? 1024 : 512) / kWave;
+    const int max_waves = (s.nch * s.cw <= 16 ? 1024 : (s.nch * s.cw <= 32 ? 512 : 256)) / kWave;
     const int64_t want = (rows + kNumCU * rpw - 1) / (kNumCU * rpw);   // waves per block for one pass
     b.waves = 4;
     while (b.waves < max_waves && b.waves < want &&
