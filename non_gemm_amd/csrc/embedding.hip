@@ -103,16 +103,24 @@ __global__ __launch_bounds__(kBlock) void emb_fwd_scalar_kernel(half_t* out, con
 // ---------------------------------------------------------------------------
 // Backward
 // ---------------------------------------------------------------------------
-// A wave takes a chunk of 64 consecutive tokens and one slice of 512 columns
-// (lane l owns the 8 consecutive columns 8l..8l+7 of the slice, so its dy
-// loads are 16 bytes and one Philox call gives its 8 dropout decisions).
-// The chunk's ids are sorted inside the wave (bitonic network over lane
-// shuffles), so the tokens of one id arrive back to back and are summed in
-// registers.  At the end of each run of equal ids the wave writes its sum
-// to LDS and reads it back transposed -- lane l then holds columns l, l+64,
-// ..., l+448 -- so every fp32 atomic add instruction covers 64 consecutive
-// floats of the dE row.  Atomics are the only cross-wave combination
-// ([LS2] sec. 2.1.2); their order is not fixed.
+// dE rows are combined with fp32 atomic adds ([LS2] sec. 2.1.2), so the
+// kernels first add up, in registers, the gradients of tokens that share an
+// id -- over as many tokens as is cheap: atomics cost about one float per
+// channel clock, and a Zipf-like id law puts a large share of the tokens on a
+// few rows, whose atomics also serialise on their addresses.
+//
+// In both kernels below a wave works on one slice of 512 columns (lane l owns
+// the 8 consecutive columns 8l..8l+7 of the slice, so its dy loads are 16
+// bytes and one Philox call gives its 8 dropout decisions) and visits tokens
+// in id order, so the tokens of one id arrive back to back.  At the end of
+// each run of equal ids the wave writes its sum to LDS and reads it back
+// transposed -- lane l then holds columns l, l+64, ..., l+448 -- so every
+// atomic add instruction covers 64 consecutive floats of the dE row.  Atomics
+// are the only combination across waves; their order is not fixed.
+//
+// Wide vocabularies (ids of 22 bits or more): a wave sorts the ids of 64
+// consecutive tokens itself (bitonic network over lane shuffles, 64-bit keys)
+// and walks all of them.
 constexpr int kChunk = 64;                // tokens per wave (one key per lane)
 constexpr int kSliceCols = kWave * 8;     // columns per wave
 constexpr int kBatch = 16;                // dy rows in flight per lane
@@ -122,6 +130,39 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
     const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
     return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Adds a run's sum (acc: this lane's 8 columns) to row id of dE, slice sl:
+// transposed through the wave's 512-float LDS buffer xp, then 8 atomic add
+// instructions of 64 consecutive floats.  Leaves acc zeroed.
+__device__ __forceinline__ void flush_row(float* dE, uint32_t id, uint32_t h, uint32_t sl, float* xp,
+                                          float (&acc)[8], int lane) {
+    float4v* w = reinterpret_cast<float4v*>(xp + lane * 8);
+    w[0] = float4v{acc[0], acc[1], acc[2], acc[3]};
+    w[1] = float4v{acc[4], acc[5], acc[6], acc[7]};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float v[8];                                       // all 8 reads, then one wait
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xp[k * kWave + lane];
+    float* row = dE + static_cast<size_t>(id) * h + static_cast<size_t>(sl) * kSliceCols;
+    const uint32_t cols = h - sl * kSliceCols;        // columns of this slice present
+    if (cols >= static_cast<uint32_t>(kSliceCols)) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) unsafeAtomicAdd(row + k * kWave + lane, v[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t c = k * kWave + lane;
+            if (c < cols) unsafeAtomicAdd(row + c, v[k]);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
 }
 
 template <bool DROP>
@@ -184,28 +225,166 @@ __global__ __launch_bounds__(kBlock) void emb_bwd_kernel(float* dE, const int32_
                 for (int k = 0; k < 8; ++k) acc[k] = fmaf(gf[k] * f[k], scale, acc[k]);
             }
             if ((ends >> pos) & 1ull) {
-                // Transpose through LDS, then coalesced atomics on the id's row.
                 const uint32_t id = static_cast<uint32_t>(readlane_u64(key, pos) >> 8);
-                float4v* w = reinterpret_cast<float4v*>(xp + lane * 8);
-                w[0] = float4v{acc[0], acc[1], acc[2], acc[3]};
-                w[1] = float4v{acc[4], acc[5], acc[6], acc[7]};
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                float* row = dE + static_cast<size_t>(id) * h + static_cast<size_t>(sl) * kSliceCols;
-                const uint32_t cols = h - sl * kSliceCols;        // columns of this slice present
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const uint32_t c = k * kWave + lane;
-                    if (c < cols) unsafeAtomicAdd(row + c, xp[c]);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+                flush_row(dE, id, h, sl, xp, acc, lane);
             }
         }
+    }
+}
+
+// Ids below 2^22: a block of kSortThreads threads takes a chunk of kSortChunk
+// consecutive tokens and one column slice, and sorts the chunk's
+// (id << 10 | position) keys in LDS.  Each of its waves then walks
+// kWavePos consecutive sorted positions, so runs are summed over up to 1024
+// tokens instead of 64 (on Zipf(1.1) ids at 8192 tokens: 3.9M atomic floats
+// instead of 6.0M, and at most 76 flushes instead of 128 on the most frequent
+// row), while 16 positions per wave keep every wave's chain of dependent
+// loads short.  Every block that works on a chunk (one per slice and group
+// of 64 positions) sorts it again: a few thousand cycles of ALU at the start
+// of each block, which keeps the call one launch without a workspace.
+constexpr int kSortThreads = 256;
+constexpr int kSortChunk = 1024;
+constexpr int kSortPer = kSortChunk / kSortThreads;      // keys per thread
+constexpr int kWavePos = 16;                             // sorted positions per wave
+constexpr int kBlockPos = kWavePos * (kSortThreads / kWave);
+constexpr int kParts = kSortChunk / kBlockPos;            // blocks per chunk and slice
+constexpr int kPosBits = 10;                              // log2(kSortChunk)
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;                  // invalid id or past the end
+constexpr int64_t kSortMaxVocab = (1ll << (32 - kPosBits)) - 1;   // ids < 2^22 - 1: keys below kNoKey
+static_assert(kSortChunk == 1 << kPosBits, "position field");
+
+// Bitonic sort, ascending, of the block's kSortChunk keys; thread t holds
+// positions kSortPer*t .. kSortPer*t + kSortPer-1 in k.  Compare-exchange
+// partners at distance j sit in the same thread (j < kSortPer), in another
+// lane of the same wave (j < kSortPer*64: one shuffle per key) or in another
+// wave (through lds, between two barriers).
+__device__ __forceinline__ uint32_t bitonic_pick(uint32_t i, uint32_t j, uint32_t size, uint32_t a,
+                                                 uint32_t b) {
+    const bool lower = (i & j) == 0, asc = (i & size) == 0;
+    return lower == asc ? min(a, b) : max(a, b);
+}
+
+__device__ __forceinline__ void block_sort_asc(uint32_t (&k)[kSortPer], uint32_t* lds) {
+    const uint32_t base = threadIdx.x * kSortPer;
+    constexpr uint32_t kWaveSpan = kSortPer * kWave;
+#pragma unroll
+    for (uint32_t size = 2; size <= kSortChunk; size <<= 1) {
+#pragma unroll
+        for (uint32_t j = size >> 1; j > 0; j >>= 1) {
+            if (j >= kWaveSpan) {
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < kSortPer; ++r) lds[base + r] = k[r];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < kSortPer; ++r) k[r] = bitonic_pick(base + r, j, size, k[r], lds[(base + r) ^ j]);
+            } else if (j >= kSortPer) {
+#pragma unroll
+                for (int r = 0; r < kSortPer; ++r) {
+                    const uint32_t o = __shfl_xor(k[r], static_cast<int>(j / kSortPer));
+                    k[r] = bitonic_pick(base + r, j, size, k[r], o);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < kSortPer; ++r) {
+                    if (r & j) continue;
+                    const uint32_t a = k[r], b = k[r | j];
+                    const bool asc = ((base + r) & size) == 0;
+                    k[r] = asc ? min(a, b) : max(a, b);
+                    k[r | j] = asc ? max(a, b) : min(a, b);
+                }
+            }
+        }
+    }
+}
+
+template <bool DROP>
+__global__ __launch_bounds__(kSortThreads) void emb_bwd_sorted_kernel(float* dE, const int32_t* ids,
+                                                                    const half_t* dy, uint32_t tokens,
+                                                                    uint32_t h, uint32_t vocab,
+                                                                    uint32_t slices, float scale,
+                                                                    Dropout d) {
+    __shared__ uint32_t keys[kSortChunk];
+    __shared__ float xpose[kSortThreads / kWave][kSliceCols];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t sl = blockIdx.x % slices, rest = blockIdx.x / slices;
+    const uint32_t part = rest % kParts, chunk = rest / kParts;
+    const uint32_t c0 = chunk * kSortChunk;
+    const uint32_t n = min(static_cast<uint32_t>(kSortChunk), tokens - c0);
+    if (part * kBlockPos >= n) return;                 // the whole block: no position of its group exists
+
+    // All id loads before the first wait: unconditional, at positions
+    // clamped to the chunk (n >= 1 here); past the end is marked afterwards.
+    int32_t raw[kSortPer];
+#pragma unroll
+    for (int r = 0; r < kSortPer; ++r) raw[r] = ids[c0 + min(threadIdx.x * kSortPer + r, n - 1)];
+    uint32_t k[kSortPer];
+#pragma unroll
+    for (int r = 0; r < kSortPer; ++r) {
+        const uint32_t pos = threadIdx.x * kSortPer + r;
+        const bool ok = pos < n && raw[r] >= 0 && static_cast<uint32_t>(raw[r]) < vocab;
+        k[r] = ok ? (static_cast<uint32_t>(raw[r]) << kPosBits) | pos : kNoKey;
+    }
+    block_sort_asc(k, keys);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortPer; ++r) keys[threadIdx.x * kSortPer + r] = k[r];
+    __syncthreads();
+
+    const uint32_t q0 = part * kBlockPos + static_cast<uint32_t>(wave) * kWavePos;
+    const uint32_t nv = h / 8;
+    const uint32_t cv = sl * kWave + lane;            // this lane's 8-column vector
+    const bool active = cv < nv;
+    float* xp = xpose[wave];
+    uint32_t key[kWavePos + 1];
+#pragma unroll
+    for (int j = 0; j <= kWavePos; ++j)
+        key[j] = __builtin_amdgcn_readfirstlane(q0 + j < kSortChunk ? keys[q0 + j] : kNoKey);
+    if (key[0] == kNoKey) return;                    // invalid keys sort last: nothing left for this wave
+
+    // Every load of the wave's tokens before the first wait: zero-filled
+    // registers, then the loads of the valid positions.
+    half8 g[kWavePos];
+#pragma unroll
+    for (int j = 0; j < kWavePos; ++j) g[j] = half8{};
+#pragma unroll
+    for (int j = 0; j < kWavePos; ++j) {
+        if (key[j] != kNoKey && active) {
+            const uint32_t t = c0 + (key[j] & (kSortChunk - 1));
+            g[j] = reinterpret_cast<const half8*>(dy + static_cast<size_t>(t) * h)[cv];
+        }
+    }
+    // The Philox words depend on the token only: computed while the loads
+    // are in flight.
+    uint32_t pw[kWavePos][4];
+    if (DROP) {
+#pragma unroll
+        for (int j = 0; j < kWavePos; ++j) {
+            const uint32_t t = c0 + (key[j] & (kSortChunk - 1));
+            if (key[j] != kNoKey) dropout_words(d, static_cast<uint64_t>(t) * nv + cv, pw[j]);
+        }
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWavePos; ++j) {
+        if (key[j] == kNoKey) break;
+        float gf[8], f[8];
+        unpack8(g[j], gf);
+        if (DROP) {
+            dropout_factors_from(d, pw[j], f);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = 1.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(gf[e] * f[e], scale, acc[e]);
+        // A run ends at the wave's last position or where the id changes
+        // (kNoKey has an id field above every valid id).
+        if (j == kWavePos - 1 || (key[j + 1] >> kPosBits) != (key[j] >> kPosBits))
+            flush_row(dE, key[j] >> kPosBits, h, sl, xp, acc, lane);
     }
 }
 
@@ -369,11 +548,23 @@ int ls_embedding_bwd(float* grad_tok_emb, const int32_t* ids, const void* dy, in
     auto* dy16 = static_cast<const half_t*>(dy);
     if (hidden % 8 == 0 && aligned16(dy)) {
         const uint32_t slices = (h32 + kSliceCols - 1) / kSliceCols;
-        const uint64_t items = static_cast<uint64_t>((t32 + kChunk - 1) / kChunk) * slices;
-        const unsigned grid = static_cast<unsigned>((items + kWaves - 1) / kWaves);
-        if (drop) emb_bwd_kernel<true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
-        else emb_bwd_kernel<false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
-        set_dispatch("embedding_bwd/chunk64_sorted_atomic");
+        if (vocab <= kSortMaxVocab) {
+            const uint64_t blocks = static_cast<uint64_t>((t32 + kSortChunk - 1) / kSortChunk) * kParts * slices;
+            if (blocks > 0x7FFFFFFFull) return fail(LS_ERR_SHAPE, "%s: tokens x hidden too large", name);
+            const unsigned grid = static_cast<unsigned>(blocks);
+            if (drop)
+                emb_bwd_sorted_kernel<true><<<grid, kSortThreads, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
+            else
+                emb_bwd_sorted_kernel<false><<<grid, kSortThreads, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
+            set_dispatch("embedding_bwd/sorted1024_atomic");
+        } else {
+            const uint64_t items = static_cast<uint64_t>((t32 + kChunk - 1) / kChunk) * slices;
+            if ((items + kWaves - 1) / kWaves > 0x7FFFFFFFull) return fail(LS_ERR_SHAPE, "%s: tokens x hidden too large", name);
+            const unsigned grid = static_cast<unsigned>((items + kWaves - 1) / kWaves);
+            if (drop) emb_bwd_kernel<true><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
+            else emb_bwd_kernel<false><<<grid, kBlock, 0, st>>>(grad_tok_emb, ids, dy16, t32, h32, v32, slices, scale, d);
+            set_dispatch("embedding_bwd/chunk64_sorted_atomic");
+        }
     } else {
         const uint64_t n = static_cast<uint64_t>(tokens) * static_cast<uint64_t>(hidden);
         const unsigned grid = grid_cap((n + kBlock - 1) / kBlock, 65536);

@@ -107,18 +107,32 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
     }
 }
 
-// Keep factors for the 8 elements 8*call .. 8*call+7: scale where kept, 0
-// where dropped.  Field j is bits [16*(j%2), 16*(j%2)+16) of word j/2.
-__device__ __forceinline__ void dropout_factors8(const Dropout& d, uint64_t call, float f[8]) {
+// The four Philox output words of call number `call` (counter = (call, offset)).
+__device__ __forceinline__ void dropout_words(const Dropout& d, uint64_t call, uint32_t w[4]) {
     uint32_t c0 = static_cast<uint32_t>(call), c1 = static_cast<uint32_t>(call >> 32);
     uint32_t c2 = d.s0, c3 = d.s1;
     philox4x32_10(c0, c1, c2, c3, d.k0, d.k1);
-    const uint32_t w[4] = {c0, c1, c2, c3};
+    w[0] = c0;
+    w[1] = c1;
+    w[2] = c2;
+    w[3] = c3;
+}
+
+// Keep factors from one call's words: scale where kept, 0 where dropped.
+// Field j is bits [16*(j%2), 16*(j%2)+16) of word j/2.
+__device__ __forceinline__ void dropout_factors_from(const Dropout& d, const uint32_t w[4], float f[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t field = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
         f[j] = field >= d.thr ? d.scale : 0.0f;
     }
+}
+
+// Keep factors for the 8 elements 8*call .. 8*call+7.
+__device__ __forceinline__ void dropout_factors8(const Dropout& d, uint64_t call, float f[8]) {
+    uint32_t w[4];
+    dropout_words(d, call, w);
+    dropout_factors_from(d, w, f);
 }
 
 // Keep factor of the single element with flat index i.

@@ -527,7 +527,7 @@ def test_embedding_c4(ls):
     assert np.all(err <= 1e-5 * mag + 1e-30), f"embedding_bwd [{last_dispatch()}]: max err {err.max()}"
     untouched = np.setdiff1d(np.arange(v), ids)
     assert np.all(got[untouched] == 0)
-    assert "chunk64" in last_dispatch()
+    assert "sorted1024" in last_dispatch()
 
 
 def _emb_bwd_check(ls, ids, dy, v, s, p, seed, off, acc=None, what=""):
@@ -547,18 +547,20 @@ def _emb_bwd_check(ls, ids, dy, v, s, p, seed, off, acc=None, what=""):
 
 
 @pytest.mark.parametrize("counts,h", [([1], 768), ([64], 768), ([65], 1024), ([2000], 768),
-                                      ([31, 33, 97, 1], 520), ([7] * 40, 1536)])
+                                      ([31, 33, 97, 1], 520), ([7] * 40, 1536), ([16, 17, 15], 512),
+                                      ([1500, 700, 3], 64), ([1] * 1100, 8)])
 def test_embedding_bwd_repeated_ids(ls, counts, h):
-    """Runs of one id inside and across 64-token chunks, column slices with
-    a ragged last slice (520, 1536 columns)."""
+    """Runs of one id inside and across the 16 sorted positions of a wave, the
+    64 of a block and the 1024 tokens of a sorted chunk; column slices with a
+    ragged last slice (520, 1536 columns)."""
     g = np.random.default_rng(sum(counts) + h)
     ids = np.concatenate([np.full(c, 5 + 3 * i, np.int32) for i, c in enumerate(counts)])
     ids = g.permutation(ids)
     pad = (-ids.size) % 4
     ids = np.concatenate([ids, np.full(pad, 2, np.int32)]).reshape(4, -1)
     dy = synth.normal16(g, (ids.size, h), 1.0)
-    disp = _emb_bwd_check(ls, ids, dy, 300, 32.0, 0.1, 21, 3, what=f"counts {counts} h={h}")
-    assert "chunk64" in disp
+    disp = _emb_bwd_check(ls, ids, dy, max(300, 5 + 3 * len(counts)), 32.0, 0.1, 21, 3, what=f"counts {counts} h={h}")
+    assert "sorted1024" in disp
 
 
 def test_embedding_bwd_other_paths(ls):
@@ -569,10 +571,16 @@ def test_embedding_bwd_other_paths(ls):
     ids = g.integers(0, 9, size=(3, 11)).astype(np.int32)             # hidden not a multiple of 8
     dy = synth.normal16(g, (ids.size, 20), 1.0)
     assert "elementwise" in _emb_bwd_check(ls, ids, dy, 9, 2.0, 0.0, 9, 3, what="hidden 20")
-    ids = g.integers(0, 1 << 20, size=(2, 300)).astype(np.int32)      # wide vocabulary, sparse hits
-    ids[0, :50] = (1 << 20) - 1
-    dy = synth.normal16(g, (ids.size, 64), 1.0)
-    _emb_bwd_check(ls, ids, dy, 1 << 20, 2.0, 0.1, 9, 3, what="vocab 2^20")
+    # The widest vocabulary of the sorted path (ids in 22 bits, below the
+    # no-key marker) and the first one past it (64-token chunks sorted by one
+    # wave with 64-bit keys); the largest id repeats across chunks.
+    for v, path in (((1 << 22) - 1, "sorted1024"), (1 << 22, "chunk64")):
+        ids = g.integers(0, v, size=(3, 700)).astype(np.int32)
+        ids[0, :50] = v - 1
+        ids[2, 100:400:3] = v - 1
+        ids[1, 5] = -1
+        dy = synth.normal16(g, (ids.size, 8), 1.0)
+        assert path in _emb_bwd_check(ls, ids, dy, v, 2.0, 0.1, 9, 3, what=f"vocab {v}")
 
 
 @pytest.mark.parametrize("b,l,h,v", [(2, 7, 64, 50), (3, 5, 768, 100), (1, 33, 24, 9), (2, 4, 20, 11),
