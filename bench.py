@@ -505,6 +505,52 @@ def summarize_counters(fetch_csv, write_csv):
     with open(COUNTERS_FILE, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
+    if f_scale and w_scale:
+        write_chain_traffic(f_rows, w_rows, f_scale, w_scale, per_kernel)
+
+
+# Kernel symbols of each chain operator (substrings of the mangled names).
+CHAIN_SYMBOLS = (
+    ("softmax_fwd", ("softmax_fwd_kernel",)),
+    ("bias_dropout_residual", ("elementwise_vec_kernelILb1ELb0ELb1E",)),       # RESID=1, RELU=0, DROP=1
+    ("layernorm_fwd", ("ln_fwd_kernel",)),
+    ("bias_relu_dropout", ("elementwise_vec_kernelILb0ELb1ELb1E",)),
+    ("layernorm_bwd", ("ln_bwd_kernel", "ln_bwd_finalize_kernel")),
+    ("softmax_bwd", ("softmax_bwd_kernel",)),
+)
+
+
+def write_chain_traffic(f_rows, w_rows, f_scale, w_scale, per_kernel):
+    """Measured HBM bytes per launch of every C3 chain kernel (FETCH_SIZE and
+    WRITE_SIZE, scaled like the dominant kernel's) against the algorithmic bytes."""
+    per, _, _ = chain_bytes(4096, 768, 3072, 12, 128)
+    out = ["# HBM traffic per launch: BERT-base layer non-GEMM chain (4096 tokens, hidden 768, FFN 3072)", "",
+           "Two `rocprofv3 --pmc` passes of `bench.py --eager` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), "
+           f"scaled by what the same counters read for torch's 1 GiB device copy in the same runs (FETCH x{f_scale:.3f}, "
+           f"WRITE x{w_scale:.3f}). Commands, from the repository root on the GPU box (R = repository root):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof_fetch "
+           "-o fetch --output-format csv -- python3 $R/bench.py --eager --steps 12 --warmup 2 --no-cpu --no-extra --no-info",
+           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof_write "
+           "-o write --output-format csv -- python3 $R/bench.py --eager --steps 12 --warmup 2 --no-cpu --no-extra --no-info",
+           "python bench.py --summarize-counters $R/gpurun_out/prof_fetch/fetch_counter_collection.csv "
+           "$R/gpurun_out/prof_write/write_counter_collection.csv", "```", "",
+           "| operator | kernel | dispatches | read MB | written MB | measured MB | algorithmic MB | measured / algorithmic |",
+           "|---|---|---|---|---|---|---|---|"]
+    for op, syms in CHAIN_SYMBOLS:
+        tot = 0.0
+        for sym in syms:
+            f, nf = per_kernel(f_rows, lambda k, s=sym: s in k)
+            w, _ = per_kernel(w_rows, lambda k, s=sym: s in k)
+            if f is None or w is None:
+                continue
+            rd, wr = f * 1024 * f_scale / 1e6, w * 1024 * w_scale / 1e6
+            tot += rd + wr
+            out.append(f"| {op} | `{sym}` | {nf} | {rd:.2f} | {wr:.2f} | {rd + wr:.2f} | | |")
+        out.append(f"| **{op}** | all | | | | **{tot:.2f}** | {per[op] / 1e6:.2f} | **{tot * 1e6 / per[op]:.3f}** |")
+    path = os.path.join(ROOT, "profiles", "chain_bert_base_4096tok_traffic.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("wrote", path)
 
 
 def stored_traffic():

@@ -24,9 +24,9 @@ constexpr int kTargetWaves = 8192;              // two 16-wave blocks per CU: fu
 constexpr int kMinRowsPerWave = 2;
 
 // Row groups: as many as keep ~kTargetWaves waves busy, at most one per 32
-// rows (every wave gets two rows: with a single row, nothing overlaps the
-// wait for it; measured 12 % slower at [4096, 768]) and at most kMaxGroups.  A function of the
-// shape only, so a workspace can be sized before the pointers are known.
+// rows (every wave gets two rows: with a single row nothing overlaps the wait
+// for it) and at most kMaxGroups.  A function of the shape only, so a
+// workspace can be sized before the pointers are known.
 inline uint32_t colsum_groups(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
     const int64_t segs = (cols + kSegCols - 1) / kSegCols;
@@ -66,8 +66,9 @@ __device__ __forceinline__ void colsum_block_fold(float* partial, const float ac
 
 // out[c] = sum over the partial rows g = 0..ngroups-1 of partial[g][c]: 16
 // thread slices per column (slice s takes rows s, s+16, ...), then the 16
-// slice sums in order.  ngroups == 0 writes zeros.
-constexpr int kFinCols = 16;
+// slice sums in order.  ngroups == 0 writes zeros.  A block takes 32 columns,
+// so each partial row is read in whole 128-byte lines.
+constexpr int kFinCols = 32;
 constexpr int kFinSlices = 16;
 static_assert(kFinSlices * 16 >= kMaxGroups, "16 loads per thread cover every partial row");
 

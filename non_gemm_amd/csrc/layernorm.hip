@@ -315,8 +315,9 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
 // Column finalisation over the [nblocks][2h] partials: column c of the 2h
 // (dgamma then dbeta) is summed by 16 thread slices (slice s takes blocks
 // s, s+16, ...), then the 16 slice sums in order.  nblocks <= 256, so every
-// thread issues at most 16 independent loads.
-constexpr int kFinCols = 16;
+// thread issues at most 16 independent loads.  A block takes 32 columns, so
+// each partial row is read in whole 128-byte lines.
+constexpr int kFinCols = 32;
 constexpr int kFinSlices = 16;
 constexpr unsigned kMaxBwdBlocks = kFinSlices * 16;
 
