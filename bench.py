@@ -202,42 +202,47 @@ def build_sets(torch, lib, shape, nsets, p, seed, eps, config=3):
 # Oracle CPU baseline
 # ---------------------------------------------------------------------------
 
+def chain_slice(inp, shape, s0, nseq):
+    """Sequences [s0, s0 + nseq) of the C3 chain inputs (parameters whole)."""
+    T0, T1 = s0 * shape.seq, (s0 + nseq) * shape.seq
+    return {k: (v[s0:s0 + nseq] if v.ndim == 4 else (v[T0:T1] if v.shape[0] == shape.tokens else v))
+            for k, v in inp.items()}
+
+
+def oracle_chain_pass(sl, shape, p, seed, eps):
+    """One pass of the oracle over every step of the chain, on a slice of it."""
+    import oracle
+    bits = 16
+    probs = oracle.softmax_fwd(sl["scores"])
+    a = oracle.bias_dropout_residual(sl["attn_proj"], sl["attn_bias"], sl["residual"], p, seed, 0, bits)
+    l1, m1, r1 = oracle.layernorm_fwd(a, sl["gamma1"], sl["beta1"], eps)
+    oracle.bias_relu_dropout(sl["ffn_pre"], sl["ffn_bias1"], p, seed, 1, bits)
+    f = oracle.bias_dropout_residual(sl["ffn_proj"], sl["ffn_bias2"], l1, p, seed, 2, bits)
+    l2, m2, r2 = oracle.layernorm_fwd(f, sl["gamma2"], sl["beta2"], eps)
+    oracle.layernorm_bwd(sl["grad_y2"], f, sl["gamma2"], m2, r2)
+    oracle.layernorm_bwd(sl["grad_y1"], a, sl["gamma1"], m1, r1)
+    k = shape.seq
+    oracle.softmax_bwd(probs.reshape(-1, k), sl["grad_probs"].reshape(-1, k))
+
+
 def cpu_baseline(shape, p, seed, eps, min_seconds=10.0, max_seconds=30.0):
     """The oracle (fp64 NumPy, single thread) over a bounded sample of the chain:
     4 of the 32 sequences (512 tokens) through every step, repeated until at
-    least `min_seconds` of CPU work; scaled to GB/s and tokens/s."""
-    import numpy as np
-
-    import oracle
+    least `min_seconds` of CPU work; scaled to GB/s and tokens/s.  Beside it,
+    the same oracle sharded by sequences over the host's cores."""
     import synth
-    bits = 16
     nseq = 4
     T = nseq * shape.seq
-    inp = synth.chain_inputs(shape, config=3)
-    sl = {k: (v[:nseq] if v.ndim == 4 else (v[:T] if v.shape[0] == shape.tokens else v)) for k, v in inp.items()}
-
-    def one_pass():
-        probs = oracle.softmax_fwd(sl["scores"])
-        a = oracle.bias_dropout_residual(sl["attn_proj"], sl["attn_bias"], sl["residual"], p, seed, 0, bits)
-        l1, m1, r1 = oracle.layernorm_fwd(a, sl["gamma1"], sl["beta1"], eps)
-        oracle.bias_relu_dropout(sl["ffn_pre"], sl["ffn_bias1"], p, seed, 1, bits)
-        f = oracle.bias_dropout_residual(sl["ffn_proj"], sl["ffn_bias2"], l1, p, seed, 2, bits)
-        l2, m2, r2 = oracle.layernorm_fwd(f, sl["gamma2"], sl["beta2"], eps)
-        oracle.layernorm_bwd(sl["grad_y2"], f, sl["gamma2"], m2, r2)
-        oracle.layernorm_bwd(sl["grad_y1"], a, sl["gamma1"], m1, r1)
-        k = shape.seq
-        oracle.softmax_bwd(probs.reshape(-1, k), sl["grad_probs"].reshape(-1, k))
-
+    sl = chain_slice(synth.chain_inputs(shape, config=3), shape, 0, nseq)
     passes = 0
     t0 = time.perf_counter()
     while True:
-        one_pass()
+        oracle_chain_pass(sl, shape, p, seed, eps)
         passes += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or el + el / passes > max_seconds:
             break
     _, _, bytes_per_pass = chain_bytes(T, shape.hidden, shape.ffn, shape.heads, shape.seq)
-    del np
     return {
         "value": round(bytes_per_pass * passes / el / 1e9, 4),
         "unit": "GB/s",
@@ -247,7 +252,66 @@ def cpu_baseline(shape, p, seed, eps, min_seconds=10.0, max_seconds=30.0):
                   f"{el:.1f} s; NumPy float64, single thread",
         "tokens_per_s": round(T * passes / el, 1),
         "host_cpus_available": len(os.sched_getaffinity(0)),
+        "all_cores": cpu_baseline_sharded(shape, seconds=min_seconds / 2),
     }
+
+
+def cpu_baseline_sharded(shape, seconds):
+    """The same oracle passes sharded by sequences over every core this process
+    may use: one single-threaded worker process per core, each on its own
+    sequences; all start together.  Throughput = all tokens over the longest
+    worker's time."""
+    import subprocess
+    n = max(1, min(len(os.sched_getaffinity(0)), shape.tokens // shape.seq))
+    per = -(-(shape.tokens // shape.seq) // n)
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    procs = []
+    for w in range(n):
+        s0 = w * per
+        cnt = min(per, shape.tokens // shape.seq - s0)
+        if cnt <= 0:
+            break
+        procs.append((cnt, subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker", str(s0), str(cnt),
+                                             str(seconds)], stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True,
+                                            env=env, cwd=ROOT)))
+    try:
+        for _, pr in procs:
+            if pr.stdout.readline().strip() != "ready":
+                raise RuntimeError("oracle worker did not start")
+        for _, pr in procs:
+            pr.stdin.write("go\n")
+            pr.stdin.flush()
+        res = [json.loads(pr.stdout.readline()) for _, pr in procs]
+    finally:
+        for _, pr in procs:
+            pr.stdin.close()
+            pr.wait(timeout=120)
+    longest = max(r["elapsed"] for r in res)
+    tokens = sum(cnt * shape.seq * r["passes"] for (cnt, _), r in zip(procs, res))
+    nbytes = sum(chain_bytes(cnt * shape.seq, shape.hidden, shape.ffn, shape.heads, shape.seq)[2] * r["passes"]
+                 for (cnt, _), r in zip(procs, res))
+    return {"value": round(nbytes / longest / 1e9, 4), "unit": "GB/s", "cores": len(procs),
+            "tokens_per_s": round(tokens / longest, 1),
+            "sample": f"{len(procs)} single-threaded worker processes, {per} sequence(s) each, "
+                      f"{min(r['passes'] for r in res)}+ passes each in {longest:.1f} s"}
+
+
+def cpu_worker(s0, nseq, seconds):
+    """One worker of cpu_baseline_sharded: builds its slice, waits for the start
+    line on stdin, runs oracle passes for `seconds`, prints the count."""
+    import synth
+    shape = synth.C3
+    sl = chain_slice(synth.chain_inputs(shape, config=3), shape, s0, nseq)
+    print("ready", flush=True)
+    sys.stdin.readline()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle_chain_pass(sl, shape, synth.DROPOUT_P, synth.DROPOUT_SEED, synth.LN_EPS)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    print(json.dumps({"passes": passes, "elapsed": el}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -698,7 +762,11 @@ def main():
                     help="launch every kernel directly instead of replaying HIP graphs (profiler runs)")
     ap.add_argument("--no-info", action="store_true", help="skip the per-kernel and warm-chain information")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--cpu-worker", nargs=3, metavar=("SEQ0", "NSEQ", "SECONDS"), help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_worker:
+        cpu_worker(int(args.cpu_worker[0]), int(args.cpu_worker[1]), float(args.cpu_worker[2]))
+        return 0
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return 0
