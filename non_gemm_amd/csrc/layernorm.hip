@@ -60,12 +60,16 @@ struct Raw;
 template <>
 struct Raw<8> {
     using T = half8;
-    // Row data (x, dy) are read once: non-temporal loads stream them past the caches.
+    // The backward's row data (dy, x) are read once: non-temporal loads
+    // stream them past the caches.
     static __device__ __forceinline__ T load(const half_t* p, size_t i) {
         return __builtin_nontemporal_load(reinterpret_cast<const half8*>(p + i));
     }
-    // gamma and beta are read by every block: a plain load keeps them cached.
-    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) {
+    // Plain loads: gamma and beta (read by every block), and the forward's x,
+    // which in a layer was just written by the kernel before it (measured in
+    // the BERT-base chain: 0.3 us per step faster than non-temporal, though
+    // 0.2 us slower on cold input).
+    static __device__ __forceinline__ T load_cached(const half_t* p, size_t i) {
         return *reinterpret_cast<const half8*>(p + i);
     }
     static __device__ __forceinline__ T zero() { return half8{0, 0, 0, 0, 0, 0, 0, 0}; }
@@ -75,7 +79,7 @@ template <>
 struct Raw<1> {
     using T = half_t;
     static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
-    static __device__ __forceinline__ T load_reused(const half_t* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ T load_cached(const half_t* p, size_t i) { return p[i]; }
     static __device__ __forceinline__ T zero() { return static_cast<half_t>(0.0f); }
     static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
 };
@@ -108,14 +112,14 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
-            if (ok && c < h) xr[j] = R::load(x, base + c);
+            if (ok && c < h) xr[j] = R::load_cached(x, base + c);
         }
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
             if (ok && c < h) {
-                gr[j] = R::load_reused(gamma, c);
-                br[j] = R::load_reused(beta, c);
+                gr[j] = R::load_cached(gamma, c);
+                br[j] = R::load_cached(beta, c);
             }
         }
         float v[NCH][CW];
@@ -197,7 +201,7 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const uint32_t c = (l + j * LPR) * CW;
-        gr[j] = c < h ? R::load_reused(gamma, c) : R::zero();
+        gr[j] = c < h ? R::load_cached(gamma, c) : R::zero();
 #pragma unroll
         for (int k = 0; k < CW; ++k) acc_g[j][k] = acc_b[j][k] = 0.0f;
     }

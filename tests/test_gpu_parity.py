@@ -343,7 +343,7 @@ def test_beam_topk_decoder_step(ls):
 
 @pytest.mark.parametrize("batch,beam,v,k", [(3, 2, 8, 2), (5, 1, 1, 1), (2, 3, 100003, 7), (4, 8, 50257, 8),
                                             (2, 4, 1000, 64), (3, 2, 600, 1000), (1, 16, 4096, 16),
-                                            (2, 5, 33, 5), (7, 3, 32768, 3)])
+                                            (2, 5, 33, 5), (7, 3, 32768, 3), (2, 4, 5000, 1024)])
 def test_beam_topk_shapes(ls, batch, beam, v, k):
     g = np.random.default_rng(batch * 7 + beam * 13 + v + k)
     lp = g.normal(size=(batch, beam, v)).astype(np.float32)
@@ -427,7 +427,7 @@ def test_layernorm_degenerate_rows(ls):
 
 SM_SHAPES = [(8, 12, 128, 128), (32, 12, 128, 128), (32, 16, 256, 256), (2, 3, 17, 64),
              (2, 2, 9, 512), (1, 2, 5, 1024), (1, 1, 3, 2048), (1, 1, 3, 4096), (1, 2, 2, 8192),
-             (1, 1, 2, 20000), (2, 2, 7, 100), (2, 3, 5, 7), (1, 1, 1, 1), (0, 12, 128, 128)]
+             (1, 1, 2, 20000), (2, 2, 7, 100), (2, 3, 5, 7), (1, 1, 1, 1), (0, 12, 128, 128), (1, 2, 3, 1023)]
 
 
 @pytest.mark.parametrize("shape", SM_SHAPES)
