@@ -158,6 +158,12 @@ __device__ __forceinline__ float xent_grad(float x, float z, uint32_t j, int32_t
     return g * (p - t);
 }
 
+// Per element: one conversion, exp2 between two FMAs,
+//   dx = g * 2^(x log2e - lse log2e) - g eps/V,
+// and - g (1 - eps) once per row, in the one vector that holds the target.
+// The gradient is computed whatever the target, then replaced for an
+// ignored (0) or invalid (NaN) one: the logits are used on every path, so
+// their load is issued with the target's and lse's, before one wait.
 __global__ __launch_bounds__(kBlock) void xent_bwd_vec_kernel(half8* dx, const half8* logits, const int32_t* targets,
                                                               const float* lse, uint32_t nvec, FastDiv nv, float g,
                                                               XentArgs a) {
@@ -168,16 +174,23 @@ __global__ __launch_bounds__(kBlock) void xent_bwd_vec_kernel(half8* dx, const h
     const uint32_t c0 = (v - row * nv.d) * 8;
     const int32_t y = targets[row];
     const float z = lse[row];
-    float o[8];
-    if (y == a.ignore) {
+    float f[8], o[8];
+    unpack8(h, f);
+    const float zl = z * kLog2e;
+    const float gb = -g * a.eps_over_v;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = 0.0f;
-    } else {
-        const bool bad = y < 0 || static_cast<uint32_t>(y) >= a.vocab;
-        float f[8];
-        unpack8(h, f);
+    for (int k = 0; k < 8; ++k) o[k] = fmaf(g, ex2(fmaf(f[k], kLog2e, -zl)), gb);
+    const uint32_t d = static_cast<uint32_t>(y) - c0;
+    if (d < 8u) {
+        const float gt = g * a.one_minus_eps;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = xent_grad(f[k], z, c0 + k, y, bad, g, a);
+        for (int k = 0; k < 8; ++k)
+            if (d == static_cast<uint32_t>(k)) o[k] -= gt;
+    }
+    if (y == a.ignore || y < 0 || static_cast<uint32_t>(y) >= a.vocab) {
+        const float r = y == a.ignore ? 0.0f : __builtin_nanf("");
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = r;
     }
     __builtin_nontemporal_store(pack8(o), dx + v);
 }
