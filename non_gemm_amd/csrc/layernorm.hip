@@ -194,44 +194,48 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
     const int sub = lane / LPR;
     extern __shared__ float lds[];     // [nwaves][2h]
 
-    // gamma stays in its fp16 form; rows are widened chunk by chunk, twice
-    // (sums, then dx), so the registers hold raw rows plus the accumulators.
-    typename R::T gr[NCH];
+    // Rows (and gamma) stay in their fp16 form and are widened chunk by
+    // chunk, twice (sums, then dx), so the registers hold raw rows plus the
+    // accumulators.
     float acc_g[NCH][CW], acc_b[NCH][CW];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        const uint32_t c = (l + j * LPR) * CW;
-        gr[j] = c < h ? R::load_cached(gamma, c) : R::zero();
+    for (int j = 0; j < NCH; ++j)
 #pragma unroll
         for (int k = 0; k < CW; ++k) acc_g[j][k] = acc_b[j][k] = 0.0f;
-    }
     const float inv_h = 1.0f / static_cast<float>(h);
     const uint32_t per_iter = static_cast<uint32_t>(nwaves) * RPW;
     const uint32_t stride = gridDim.x * per_iter;
     const uint32_t my = static_cast<uint32_t>(wave) * RPW + sub;
 
-    // Loads of one row: raw fp16 chunks and the saved statistics.
-    typename R::T rdy[NCH], rx[NCH];
+    // Loads of one row: raw fp16 chunks, gamma (a cache hit, loaded again
+    // with every row: kept from before the row loop, the wait for it would
+    // come before the row's loads are issued) and the saved statistics.
+    typename R::T rdy[NCH], rx[NCH], gr[NCH];
     float mu = 0.0f, rs = 0.0f;
-    auto fetch = [&](uint32_t row, typename R::T* ody, typename R::T* ox, float& omu, float& ors) {
+    auto fetch = [&](uint32_t row) {
         const bool ok = row < rows;
         const size_t base = static_cast<size_t>(row) * h;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) ody[j] = ox[j] = R::zero();
+        for (int j = 0; j < NCH; ++j) rdy[j] = rx[j] = gr[j] = R::zero();
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const uint32_t c = (l + j * LPR) * CW;
             if (ok && c < h) {
-                ody[j] = R::load(dy, base + c);
-                ox[j] = R::load(x, base + c);
+                rdy[j] = R::load(dy, base + c);
+                rx[j] = R::load(x, base + c);
             }
         }
-        omu = ok ? mean[row] : 0.0f;
-        ors = ok ? rstd[row] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            if (ok && c < h) gr[j] = R::load_cached(gamma, c);
+        }
+        mu = ok ? mean[row] : 0.0f;
+        rs = ok ? rstd[row] : 0.0f;
     };
     for (uint32_t r0 = blockIdx.x * per_iter; r0 < rows; r0 += stride) {
         const uint32_t row = r0 + my;
-        fetch(row, rdy, rx, mu, rs);
+        fetch(row);
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
