@@ -18,6 +18,8 @@
 // per chunk; CW = 1: the element-wise path for unaligned rows).  Chunk j of
 // lane l starts at column (l + j*LPR)*CW, so at every j the LPR lanes of a
 // row read one contiguous span.
+#include <type_traits>
+
 #include "ls_common.hpp"
 
 namespace ls {
@@ -75,8 +77,24 @@ struct Raw<8> {
     static __device__ __forceinline__ T zero() { return half8{0, 0, 0, 0, 0, 0, 0, 0}; }
     static __device__ __forceinline__ void widen(const T& r, float f[8]) { unpack8(r, f); }
 };
+// One fp16 element per 32-bit register (zero-extended): fp16 values kept two
+// to a register would need each load merged into its pair as it arrives, a
+// wait per element.
 template <>
 struct Raw<1> {
+    using T = uint32_t;
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) {
+        return reinterpret_cast<const uint16_t*>(p)[i];
+    }
+    static __device__ __forceinline__ T load_cached(const half_t* p, size_t i) { return load(p, i); }
+    static __device__ __forceinline__ T zero() { return 0u; }
+    static __device__ __forceinline__ void widen(const T& r, float f[1]) {
+        f[0] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(r)));
+    }
+};
+// Two fp16 elements per register: the element-wise backward for rows of more
+// than 2048 elements, where one element per register does not fit.
+struct RawHalf {
     using T = half_t;
     static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
     static __device__ __forceinline__ T load_cached(const half_t* p, size_t i) { return p[i]; }
@@ -107,19 +125,42 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
         // The row's chunks first, then gamma and beta (cache hits after the
         // first waves); one wait covers all of them.
         typename R::T xr[NCH], gr[NCH], br[NCH];
+        if constexpr (CW == 1) {
+            // Element-wise path: unconditional loads at indices clamped into
+            // the tensor, out-of-range values zeroed afterwards (a load
+            // under a branch gets its conversion moved into the branch, a
+            // wait per element).
+            const size_t cbase = static_cast<size_t>(ok ? row : rows - 1) * h;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) xr[j] = gr[j] = br[j] = R::zero();
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = l + j * LPR;
+                const uint32_t cc = c < h ? c : h - 1;
+                xr[j] = R::load_cached(x, cbase + cc);
+                gr[j] = R::load_cached(gamma, cc);
+                br[j] = R::load_cached(beta, cc);
+            }
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (ok && c < h) xr[j] = R::load_cached(x, base + c);
-        }
+            for (int j = 0; j < NCH; ++j) {
+                const bool in = ok && l + j * LPR < h;
+                xr[j] = in ? xr[j] : R::zero();
+                gr[j] = in ? gr[j] : R::zero();
+                br[j] = in ? br[j] : R::zero();
+            }
+        } else {
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (ok && c < h) {
-                gr[j] = R::load_cached(gamma, c);
-                br[j] = R::load_cached(beta, c);
+            for (int j = 0; j < NCH; ++j) xr[j] = gr[j] = br[j] = R::zero();
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                if (ok && c < h) xr[j] = R::load_cached(x, base + c);
+            }
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                if (ok && c < h) {
+                    gr[j] = R::load_cached(gamma, c);
+                    br[j] = R::load_cached(beta, c);
+                }
             }
         }
         float v[NCH][CW];
@@ -173,9 +214,15 @@ __global__ __launch_bounds__(kBlock) void ln_fwd_kernel(half_t* y, float* mean, 
 // (<= 128 VGPRs), 8 up to 32 elements, 4 beyond (one wave per SIMD, up to 512
 // VGPRs, so the largest rows do not spill); the wave slots of the column fold
 // take at most 128 KiB of LDS.
+// The element-wise path (CW = 1) holds every element of a row in a register
+// of its own (up to 32 per lane), so it takes smaller blocks.
+constexpr int bwd_max_threads(int nch, int cw) {
+    return cw == 1 ? (nch <= 8 ? 1024 : (nch <= 16 ? 512 : 256))
+                   : (nch * cw <= 16 ? 1024 : (nch * cw <= 32 ? 512 : 256));
+}
 template <int NCH, int CW>
 struct BwdBounds {
-    static constexpr int kMaxThreads = NCH * CW <= 16 ? 1024 : (NCH * CW <= 32 ? 512 : 256);
+    static constexpr int kMaxThreads = bwd_max_threads(NCH, CW);
 };
 constexpr size_t kBwdLdsBudget = 128 * 1024;
 
@@ -185,7 +232,10 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
                                                                 const half_t* gamma, const float* mean,
                                                                 const float* rstd, uint32_t rows,
                                                                 uint32_t h) {
-    using R = Raw<CW>;
+    // Element-wise rows of up to 2048: one register per element and clamped
+    // unconditional loads; longer ones: packed registers.
+    constexpr bool kClamped = CW == 1 && NCH <= 32;
+    using R = std::conditional_t<(CW == 1 && !kClamped), RawHalf, Raw<CW>>;
     constexpr int RPW = kWave / LPR;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -214,24 +264,50 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
     float mu = 0.0f, rs = 0.0f;
     auto fetch = [&](uint32_t row) {
         const bool ok = row < rows;
-        const size_t base = static_cast<size_t>(row) * h;
+        if constexpr (kClamped) {
+            // Element-wise path: unconditional loads at clamped indices, as in
+            // the forward.
+            const uint32_t rc = ok ? row : rows - 1;
+            const size_t cbase = static_cast<size_t>(rc) * h;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) rdy[j] = rx[j] = gr[j] = R::zero();
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (ok && c < h) {
-                rdy[j] = R::load(dy, base + c);
-                rx[j] = R::load(x, base + c);
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = l + j * LPR;
+                const uint32_t cc = c < h ? c : h - 1;
+                rdy[j] = R::load(dy, cbase + cc);
+                rx[j] = R::load(x, cbase + cc);
+                gr[j] = R::load_cached(gamma, cc);
             }
-        }
+            mu = mean[rc];
+            rs = rstd[rc];
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (ok && c < h) gr[j] = R::load_cached(gamma, c);
+            for (int j = 0; j < NCH; ++j) {
+                const bool in = ok && l + j * LPR < h;
+                rdy[j] = in ? rdy[j] : R::zero();
+                rx[j] = in ? rx[j] : R::zero();
+                gr[j] = in ? gr[j] : R::zero();
+            }
+            mu = ok ? mu : 0.0f;
+            rs = ok ? rs : 0.0f;
+        } else {
+            const size_t base = static_cast<size_t>(row) * h;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) rdy[j] = rx[j] = gr[j] = R::zero();
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                if (ok && c < h) {
+                    rdy[j] = R::load(dy, base + c);
+                    rx[j] = R::load(x, base + c);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                if (ok && c < h) gr[j] = R::load_cached(gamma, c);
+            }
+            mu = ok ? mean[row] : 0.0f;
+            rs = ok ? rstd[row] : 0.0f;
         }
-        mu = ok ? mean[row] : 0.0f;
-        rs = ok ? rstd[row] : 0.0f;
     };
     for (uint32_t r0 = blockIdx.x * per_iter; r0 < rows; r0 += stride) {
         const uint32_t row = r0 + my;
@@ -408,7 +484,7 @@ struct BwdLaunch {
 BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
     BwdLaunch b;
     const int64_t rpw = kWave / s.lpr;
-    const int max_waves = (s.nch * s.cw <= 16 ? 1024 : (s.nch * s.cw <= 32 ? 512 : 256)) / kWave;
+    const int max_waves = bwd_max_threads(s.nch, s.cw) / kWave;
     const int64_t want = (rows + kNumCU * rpw - 1) / (kNumCU * rpw);   // waves per block for one pass
     b.waves = 4;
     while (b.waves < max_waves && b.waves < want &&

@@ -46,12 +46,20 @@ struct Chunk<8> {
         __builtin_nontemporal_store(pack8(f), reinterpret_cast<half8*>(p + i));
     }
 };
+// Element-wise path: one fp16 element per 32-bit register (zero-extended);
+// two to a register would need each load merged into its pair as it arrives.
 template <>
 struct Chunk<1> {
-    using T = half_t;
-    static __device__ __forceinline__ T fill(float v) { return static_cast<half_t>(v); }
-    static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
-    static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
+    using T = uint32_t;
+    static __device__ __forceinline__ T fill(float v) {
+        return __builtin_bit_cast(uint16_t, static_cast<half_t>(v));
+    }
+    static __device__ __forceinline__ T load(const half_t* p, size_t i) {
+        return reinterpret_cast<const uint16_t*>(p)[i];
+    }
+    static __device__ __forceinline__ void widen(const T& r, float f[1]) {
+        f[0] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(r)));
+    }
     static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[1]) {
         p[i] = static_cast<half_t>(f[0]);
     }
@@ -95,15 +103,45 @@ __global__ __launch_bounds__(kBlock) void softmax_fwd_kernel(half_t* y, const ha
     for (uint32_t r0 = blockIdx.x * (kWaves * RPW); r0 < rows; r0 += gridDim.x * (kWaves * RPW)) {
         const uint32_t row = r0 + wave * RPW + sub;
         const bool ok = row < rows;
-        const uint32_t n = ok ? valid_keys<MASKED>(mask, row, k) : 0u;
         const size_t base = static_cast<size_t>(row) * k;
         typename Chunk<CW>::T raw[NCH];
+        uint32_t n;
+        if constexpr (CW == 1) {
+            // Element-wise path: unconditional loads at indices clamped into
+            // the tensor (issued before the key length is read), then -inf
+            // past the valid keys (a load under a branch gets its conversion
+            // moved into the branch: a wait per element).
+            const size_t cbase = static_cast<size_t>(ok ? row : rows - 1) * k;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) raw[j] = Chunk<CW>::fill(-INFINITY);
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = l + j * LPR;
+                raw[j] = Chunk<CW>::load(x, cbase + (c < k ? c : k - 1));
+            }
+            n = ok ? valid_keys<MASKED>(mask, row, k) : 0u;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (c < n) raw[j] = Chunk<CW>::load(x, base + c);
+            for (int j = 0; j < NCH; ++j) raw[j] = l + j * LPR < n ? raw[j] : Chunk<CW>::fill(-INFINITY);
+        } else if constexpr (!MASKED) {
+            // Every key valid: unconditional loads, chunks past the row end
+            // redirected to its last vector (a cache hit) and set to -inf.
+            n = ok ? k : 0u;
+            const size_t cbase = static_cast<size_t>(ok ? row : rows - 1) * k;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                raw[j] = Chunk<CW>::load(x, cbase + (c < k ? c : k - CW));
+            }
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) raw[j] = (l + j * LPR) * CW < n ? raw[j] : Chunk<CW>::fill(-INFINITY);
+        } else {
+            // Masked rows: keys past the row's length are not read at all.
+            n = ok ? valid_keys<MASKED>(mask, row, k) : 0u;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) raw[j] = Chunk<CW>::fill(-INFINITY);
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                if (c < n) raw[j] = Chunk<CW>::load(x, base + c);
+            }
         }
         float v[NCH][CW];
 #pragma unroll
@@ -155,14 +193,23 @@ __global__ __launch_bounds__(kBlock) void softmax_bwd_kernel(half_t* dx, const h
         const bool ok = row < rows;
         const size_t base = static_cast<size_t>(row) * k;
         typename Chunk<CW>::T ry[NCH], rd[NCH];
+        {
+            // Unconditional loads at indices clamped into the tensor (chunks
+            // past the row end re-read its last one, a cache hit), zeroed
+            // afterwards: a load under a branch can get a wait of its own.
+            const size_t cbase = static_cast<size_t>(ok ? row : rows - 1) * k;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) ry[j] = rd[j] = Chunk<CW>::fill(0.0f);
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                const size_t i = cbase + (c < k ? c : k - CW);
+                ry[j] = Chunk<CW>::load(y, i);
+                rd[j] = Chunk<CW>::load(dy, i);
+            }
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (ok && c < k) {
-                ry[j] = Chunk<CW>::load(y, base + c);
-                rd[j] = Chunk<CW>::load(dy, base + c);
+            for (int j = 0; j < NCH; ++j) {
+                const bool in = ok && (l + j * LPR) * CW < k;
+                ry[j] = in ? ry[j] : Chunk<CW>::fill(0.0f);
+                rd[j] = in ? rd[j] : Chunk<CW>::fill(0.0f);
             }
         }
         float vy[NCH][CW], vd[NCH][CW];
@@ -229,12 +276,25 @@ __global__ __launch_bounds__(kBigBlock) void softmax_fwd_block_kernel(half_t* y,
         const uint32_t n = valid_keys<MASKED>(mask, row, k);
         const size_t base = static_cast<size_t>(row) * k;
         half8 raw[NCH];
+        if constexpr (!MASKED) {
+            // Every key valid: unconditional loads (past the row end: its last
+            // vector again), then -inf there.
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) raw[j] = Chunk<8>::fill(-INFINITY);
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (threadIdx.x + j * kBigBlock) * 8;
+                raw[j] = Chunk<8>::load(x, base + (c < k ? c : k - 8));
+            }
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (threadIdx.x + j * kBigBlock) * 8;
-            if (c < n) raw[j] = Chunk<8>::load(x, base + c);
+            for (int j = 0; j < NCH; ++j)
+                raw[j] = (threadIdx.x + j * kBigBlock) * 8 < n ? raw[j] : Chunk<8>::fill(-INFINITY);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) raw[j] = Chunk<8>::fill(-INFINITY);
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (threadIdx.x + j * kBigBlock) * 8;
+                if (c < n) raw[j] = Chunk<8>::load(x, base + c);
+            }
         }
         float v[NCH][8];
         float m = -INFINITY;
