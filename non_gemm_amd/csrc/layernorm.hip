@@ -92,16 +92,6 @@ struct Raw<1> {
         f[0] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(r)));
     }
 };
-// Two fp16 elements per register: the element-wise backward for rows of more
-// than 2048 elements, where one element per register does not fit.
-struct RawHalf {
-    using T = half_t;
-    static __device__ __forceinline__ T load(const half_t* p, size_t i) { return p[i]; }
-    static __device__ __forceinline__ T load_cached(const half_t* p, size_t i) { return p[i]; }
-    static __device__ __forceinline__ T zero() { return static_cast<half_t>(0.0f); }
-    static __device__ __forceinline__ void widen(const T& r, float f[1]) { f[0] = static_cast<float>(r); }
-};
-
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
@@ -233,9 +223,10 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
                                                                 const float* rstd, uint32_t rows,
                                                                 uint32_t h) {
     // Element-wise rows of up to 2048: one register per element and clamped
-    // unconditional loads; longer ones: packed registers.
+    // unconditional loads; longer ones are read twice (kTwoPass).
     constexpr bool kClamped = CW == 1 && NCH <= 32;
-    using R = std::conditional_t<(CW == 1 && !kClamped), RawHalf, Raw<CW>>;
+    constexpr bool kTwoPass = CW == 1 && NCH > 32;
+    using R = Raw<CW>;
     constexpr int RPW = kWave / LPR;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -247,9 +238,11 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
     // Rows (and gamma) stay in their fp16 form and are widened chunk by
     // chunk, twice (sums, then dx), so the registers hold raw rows plus the
     // accumulators.
-    float acc_g[NCH][CW], acc_b[NCH][CW];
+    // (The two-pass path keeps its column sums in the wave's LDS slot.)
+    constexpr int NACC = kTwoPass ? 1 : NCH;
+    float acc_g[NACC][CW], acc_b[NACC][CW];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j)
+    for (int j = 0; j < NACC; ++j)
 #pragma unroll
         for (int k = 0; k < CW; ++k) acc_g[j][k] = acc_b[j][k] = 0.0f;
     const float inv_h = 1.0f / static_cast<float>(h);
@@ -309,6 +302,86 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
             rs = ok ? rstd[row] : 0.0f;
         }
     };
+    if constexpr (kTwoPass) {
+        // Element-wise rows longer than 2048: each row is read twice, in
+        // batches of kB elements per lane -- sums, then dx from the caches --
+        // and the column sums live in the wave's LDS slot [dgamma | dbeta],
+        // where lane l owns columns l, l + 64, ... (no other lane touches them).
+        constexpr int kB = 32;                  // two batches per pass
+        static_assert(NCH % kB == 0, "whole batches");
+        static_assert(LPR == kWave, "one row per wave");
+        float* mine = lds + static_cast<size_t>(wave) * 2 * h;
+        for (uint32_t c = l; c < h; c += LPR) mine[c] = mine[h + c] = 0.0f;
+        for (uint32_t r0 = blockIdx.x * per_iter; r0 < rows; r0 += stride) {
+            const uint32_t row = r0 + my;
+            const bool ok = row < rows;
+            const uint32_t rc = ok ? row : rows - 1;
+            const size_t cbase = static_cast<size_t>(rc) * h;
+            float sa = 0.0f, sb = 0.0f;
+            const float m0 = ok ? mean[rc] : 0.0f, s0 = ok ? rstd[rc] : 0.0f;
+#pragma unroll 1
+            for (int b0 = 0; b0 < NCH; b0 += kB) {
+                uint32_t ud[kB], ux[kB], ug[kB];
+#pragma unroll
+                for (int i = 0; i < kB; ++i) {
+                    const uint32_t c = l + (b0 + i) * LPR;
+                    const uint32_t cc = c < h ? c : h - 1;
+                    ud[i] = R::load_cached(dy, cbase + cc);
+                    ux[i] = R::load_cached(x, cbase + cc);
+                    ug[i] = R::load_cached(gamma, cc);
+                }
+#pragma unroll
+                for (int i = 0; i < kB; ++i) {
+                    const bool in = ok && l + (b0 + i) * LPR < h;
+                    float fd, fx, fg;
+                    R::widen(ud[i], &fd);
+                    R::widen(ux[i], &fx);
+                    R::widen(ug[i], &fg);
+                    fd = in ? fd : 0.0f;
+                    fx = in ? fx : 0.0f;
+                    fg = in ? fg : 0.0f;
+                    const float xh = (fx - m0) * s0;
+                    const float gd = fg * fd;
+                    sa += gd;
+                    sb = fmaf(gd, xh, sb);
+                    const uint32_t c = l + (b0 + i) * LPR;
+                    if (in) {
+                        mine[c] = fmaf(fd, xh, mine[c]);
+                        mine[h + c] += fd;
+                    }
+                }
+            }
+            sa = group_sum<LPR>(sa);
+            sb = group_sum<LPR>(sb);
+            const float ca = sa * inv_h, cb = sb * inv_h;
+            if (ok) {
+#pragma unroll 1
+                for (int b0 = 0; b0 < NCH; b0 += kB) {
+                    uint32_t ud[kB], ux[kB], ug[kB];
+#pragma unroll
+                    for (int i = 0; i < kB; ++i) {
+                        const uint32_t c = l + (b0 + i) * LPR;
+                        const uint32_t cc = c < h ? c : h - 1;
+                        ud[i] = R::load_cached(dy, cbase + cc);
+                        ux[i] = R::load_cached(x, cbase + cc);
+                        ug[i] = R::load_cached(gamma, cc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < kB; ++i) {
+                        const uint32_t c = l + (b0 + i) * LPR;
+                        if (c < h) {
+                            float fd, fx, fg, o;
+                            R::widen(ud[i], &fd);
+                            R::widen(ux[i], &fx);
+                            R::widen(ug[i], &fg);
+                            o = s0 * (fg * fd - fmaf((fx - m0) * s0, cb, ca));
+                            Chunk<1>::store(dx, cbase + c, &o);
+                        }
+                    }
+                }
+            }
+        }
+    } else {
     for (uint32_t r0 = blockIdx.x * per_iter; r0 < rows; r0 += stride) {
         const uint32_t row = r0 + my;
         fetch(row);
@@ -350,7 +423,9 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
             }
         }
     }
+    }
 
+    if constexpr (!kTwoPass) {
     // Fold the RPW row groups of this wave (lanes l, l+LPR, ... own the same columns).
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -386,6 +461,7 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
                 }
             }
         }
+    }
     }
     __syncthreads();
     float* out = partial + static_cast<size_t>(blockIdx.x) * 2 * h;
@@ -474,7 +550,8 @@ unsigned fwd_grid(int64_t rows, const LnShape& s) {
 
 // Backward launch: waves per block (a power of two, 4 up to the shape's
 // register and LDS limits) so that about one block per CU covers every row,
-// then the block count (at most 256).
+// then the block count (at most 256).  (Blocks of fewer waves for few rows
+// measured slower: each block adds a partial row of 2h floats.)
 struct BwdLaunch {
     int waves;
     unsigned grid;
