@@ -201,6 +201,8 @@ __global__ __launch_bounds__(kBlock) void emb_bwd_kernel(float* dE, const int32_
         half8 g[kBatch];
         uint32_t tk[kBatch];
 #pragma unroll
+        for (int j = 0; j < kBatch; ++j) g[j] = half8{};      // filled first: the loads stay in flight
+#pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             tk[j] = 0;
             if (b0 + j < count) {

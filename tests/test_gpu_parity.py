@@ -369,7 +369,8 @@ def test_beam_topk_ties_special_values_and_overflow(ls):
 # ----------------------------------------------------------------------------
 
 LN_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (1000, 64), (77, 96), (33, 512), (9, 1536),
-             (5, 2048), (3, 4096), (50, 100), (20, 13), (1, 8), (300, 768), (4, 4095)]
+             (5, 2048), (3, 4096), (50, 100), (20, 13), (1, 8), (300, 768), (4, 4095),
+             (300, 2047), (64, 3001), (1030, 767)]
 
 
 def ln_inputs(rows, h, seed):
@@ -427,7 +428,8 @@ def test_layernorm_degenerate_rows(ls):
 
 SM_SHAPES = [(8, 12, 128, 128), (32, 12, 128, 128), (32, 16, 256, 256), (2, 3, 17, 64),
              (2, 2, 9, 512), (1, 2, 5, 1024), (1, 1, 3, 2048), (1, 1, 3, 4096), (1, 2, 2, 8192),
-             (1, 1, 2, 20000), (2, 2, 7, 100), (2, 3, 5, 7), (1, 1, 1, 1), (0, 12, 128, 128), (1, 2, 3, 1023)]
+             (1, 1, 2, 20000), (2, 2, 7, 100), (2, 3, 5, 7), (1, 1, 1, 1), (0, 12, 128, 128), (1, 2, 3, 1023),
+             (3, 5, 9, 1000), (2, 3, 4, 2000)]
 
 
 @pytest.mark.parametrize("shape", SM_SHAPES)
