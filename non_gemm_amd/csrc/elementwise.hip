@@ -124,7 +124,9 @@ int launch_elementwise(const char* name, void* out, const void* x, const void* b
     if (vec) {
         const uint32_t nvec = static_cast<uint32_t>(n / 8);
         const FastDiv cv(static_cast<uint32_t>(cols / 8));
-        const unsigned grid = grid_for(nvec, kBlock, kGridCap);
+        // Below 2M vectors (32 MB of output) half the cap: measured 2 % faster on [4096, 3072]
+        // and 0.3 us per BERT-base chain step; the larger Transformer-big shapes keep the full cap.
+        const unsigned grid = grid_for(nvec, kBlock, nvec < (2u << 20) ? kGridCap / 2 : kGridCap);
         auto* o = static_cast<half8*>(out);
         auto* xv = static_cast<const half8*>(x);
         auto* bv = static_cast<const half8*>(bias);
