@@ -258,7 +258,7 @@ static_assert(kSortChunk == 1 << kPosBits, "position field");
 // Bitonic sort, ascending, of the block's kSortChunk keys; thread t holds
 // positions kSortPer*t .. kSortPer*t + kSortPer-1 in k.  Compare-exchange
 // partners at distance j sit in the same thread (j < kSortPer), in another
-// lane of the same wave (j < kSortPer*64: one shuffle per key) or in another
+// lane of the same wave (j < kSortPer*64: one DPP / swizzle / permute per key) or in another
 // wave (through lds, between two barriers).
 __device__ __forceinline__ uint32_t bitonic_pick(uint32_t i, uint32_t j, uint32_t size, uint32_t a,
                                                  uint32_t b) {
@@ -283,7 +283,7 @@ __device__ __forceinline__ void block_sort_asc(uint32_t (&k)[kSortPer], uint32_t
             } else if (j >= kSortPer) {
 #pragma unroll
                 for (int r = 0; r < kSortPer; ++r) {
-                    const uint32_t o = __shfl_xor(k[r], static_cast<int>(j / kSortPer));
+                    const uint32_t o = lane_xor_u32(k[r], j / kSortPer);
                     k[r] = bitonic_pick(base + r, j, size, k[r], o);
                 }
             } else {

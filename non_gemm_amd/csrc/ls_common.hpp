@@ -166,6 +166,21 @@ __device__ __forceinline__ float swz_xor16(float v) {
 }
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
+// v from lane (lane ^ m), m a power of two below 64 (a constant after
+// unrolling): DPP for 1 and 2, ds_swizzle (no LDS access) for 4..16, and
+// ds_bpermute only across the two 32-lane halves.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, uint32_t m) {
+    const int x = static_cast<int>(v);
+    switch (m) {
+        case 1: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, kDppXor1, 0xF, 0xF, false));
+        case 2: return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, kDppXor2, 0xF, 0xF, false));
+        case 4: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(x, 0x101F));
+        case 8: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(x, 0x201F));
+        case 16: return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(x, 0x401F));
+        default: return static_cast<uint32_t>(__shfl_xor(x, static_cast<int>(m)));
+    }
+}
+
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
     static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
