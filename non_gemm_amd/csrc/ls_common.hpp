@@ -208,8 +208,8 @@ __device__ __forceinline__ float group_max(float v) {
 // 64-bit lane exchange, and an ascending bitonic sort of one 64-bit key per
 // lane across the whole wave (lane 0 ends with the smallest key).
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+    const uint32_t lo = lane_xor_u32(static_cast<uint32_t>(v), static_cast<uint32_t>(m));
+    const uint32_t hi = lane_xor_u32(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(m));
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 __device__ __forceinline__ uint64_t wave_sort_asc(uint64_t key, int lane) {
