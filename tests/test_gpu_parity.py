@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 from conftest import fp16_mismatch
+from golden_data import hars_example
 
 pytestmark = pytest.mark.gpu
 
@@ -331,6 +332,13 @@ def check_topk(ls, lp, bs, k, what):
     assert np.array_equal(got_s[~nan].view(np.uint32), ref_s[~nan].view(np.uint32)), what
 
 
+def test_beam_topk_golden_example(ls):
+    """The beam 2 x vocabulary 8 example of the HARS slides (fixture in
+    tests/golden/): the kernel returns the oracle's top-k."""
+    lp, k, _, _ = hars_example()
+    check_topk(ls, lp, None, k, "beam_topk golden beam 2 x vocab 8")
+
+
 def test_beam_topk_decoder_step(ls):
     """Transformer-big decoder step: 128 sentences x beam 4 over vocab 32768."""
     g = np.random.default_rng(17)
@@ -405,6 +413,27 @@ def test_layernorm_bwd(ls, rows, h):
     dx2, dg2, db2 = ls.layernorm_bwd(dev(dy), dev(x), dev(gamma), dev(mean), dev(rstd))
     assert np.array_equal(host(dg2), host(dg)) and np.array_equal(host(db2), host(db))
     assert np.array_equal(host(dx2), host(dx))
+
+
+def test_layernorm_bwd_workspace_reuse(ls):
+    """One workspace serves calls of different shapes in turn (different
+    block counts, so different partial-row layouts): each call is
+    bit-identical to a call on a fresh workspace and matches the oracle."""
+    shapes = [(4096, 768), (300, 768), (77, 96), (8192, 1024), (1, 8), (4096, 768)]
+    need = max(ls.layernorm_bwd_workspace_bytes(r, h) for r, h in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")    # stale contents are ignored
+    for i, (rows, h) in enumerate(shapes):
+        x, gamma, beta, dy = ln_inputs(rows, h, 11 + i)
+        _, mean, rstd = oracle.layernorm_fwd(x, gamma, beta, synth.LN_EPS)
+        args = (dev(dy), dev(x), dev(gamma), dev(mean), dev(rstd))
+        got = ls.layernorm_bwd(*args, workspace=ws)
+        tag = f"layernorm_bwd reuse {rows}x{h} [{last_dispatch()}]"
+        fresh = ls.layernorm_bwd(*args)
+        for a, b in zip(got, fresh):
+            assert np.array_equal(host(a), host(b)), tag
+        rdx, rdg, rdb = oracle.layernorm_bwd(dy, x, gamma, mean, rstd)
+        assert_fp16(host(got[1]), rdg, tag + " dgamma")
+        assert_fp16(host(got[2]), rdb, tag + " dbeta")
 
 
 def test_layernorm_degenerate_rows(ls):
