@@ -653,7 +653,7 @@ def test_embedding_invalid_ids(ls):
 
 @pytest.mark.parametrize("n,decoupled,offset,steps", [(1_000_003, True, 0, 10), (77, True, 0, 10),
                                                       (50_001, True, 3, 10), (4096, False, 0, 1),
-                                                      (4096, False, 0, 10)])
+                                                      (4096, False, 0, 10), (2052, True, 0, 3)])
 def test_adam_steps(ls, n, decoupled, offset, steps):
     """AdamW (the workspace trainer's mode): moments depend on the gradient
     only, so they meet the fp32 bar over all ten steps.  L2 mode feeds the
