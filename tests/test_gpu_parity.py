@@ -156,11 +156,11 @@ def test_nan_inf_propagate(ls):
 # Backward of the fused elementwise operators
 # ----------------------------------------------------------------------------
 
-# full C3/C4 shapes, several 512-column segments with ragged last ones, the
-# element-wise path (cols % 8 != 0), one row, row counts that leave the last
-# row group short
-EW_BWD_SHAPES = [(4096, 768), (4096, 3072), (8192, 1024), (129, 520), (1000, 4104), (37, 24), (1, 8),
-                 (3, 13), (300, 20), (17, 1)]
+# full C3/C4 shapes, several 512-column segments with ragged last ones (384,
+# 520, 768, 4104 columns), the element-wise path (cols % 8 != 0), one row,
+# row counts that leave the last row group short
+EW_BWD_SHAPES = [(4096, 768), (4096, 3072), (8192, 1024), (200, 384), (333, 768), (129, 520), (1000, 4104),
+                 (37, 24), (1, 8), (3, 13), (300, 20), (17, 1)]
 
 
 @pytest.mark.parametrize("rows,cols", EW_BWD_SHAPES)
