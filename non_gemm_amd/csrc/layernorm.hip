@@ -583,8 +583,8 @@ BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
                                 hipFuncAttributeMaxDynamicSharedMemorySize,                    \
                                 static_cast<int>(bl.lds_bytes)) != hipSuccess)                  \
             return fail(LS_ERR_HIP, "%s: cannot reserve %zu bytes of LDS", name, bl.lds_bytes); \
-        ln_bwd_kernel<LPR, NCH, CW><<<bl.grid, bl.waves * kWave, bl.lds_bytes, st>>>(          \
-            dx16, part, dy16, x16, g16, mean, rstd, r32, h32);                                  \
+        launch_kernel(ln_bwd_kernel<LPR, NCH, CW>, dim3(bl.grid), dim3(bl.waves * kWave),         \
+                      bl.lds_bytes, st, dx16, part, dy16, x16, g16, mean, rstd, r32, h32);         \
     } while (0)
 
 #define LS_LN_TABLE(M)                                                                          \
