@@ -781,6 +781,81 @@ def test_probe_copy_and_read(ls, nbytes):
 # eager result bit for bit (no memset nodes, no state carried between calls)
 # ----------------------------------------------------------------------------
 
+CHAIN_CONFIGS = [(1, synth.C1), (3, synth.C3), (4, synth.C4)]
+
+
+@pytest.mark.parametrize("config,shape", CHAIN_CONFIGS, ids=["tiny-128x256", "bert-base", "transformer-big"])
+def test_layer_chain_configs(ls, config, shape):
+    """A configured layer chain end to end, from the config's seeded inputs:
+    every GPU operator consumes the GPU outputs of the one before it, the
+    oracle its own outputs (dropout 0.1 at the three sites, LayerNorm eps
+    1e-5), and every output is held to the fp16 / fp32 bars."""
+    inp = synth.chain_inputs(shape, config=config)
+    p, eps = synth.DROPOUT_P, synth.LN_EPS
+    g = {k: dev(v) for k, v in inp.items()}
+    probs = ls.softmax_fwd(g["scores"])
+    a = ls.bias_dropout_residual(g["attn_proj"], g["attn_bias"], g["residual"], p, SEED, synth.SITE_ATTN_OUT)
+    l1, m1, r1 = ls.layernorm_fwd(a, g["gamma1"], g["beta1"], eps)
+    act = ls.bias_relu_dropout(g["ffn_pre"], g["ffn_bias1"], p, SEED, synth.SITE_FFN_ACT)
+    f = ls.bias_dropout_residual(g["ffn_proj"], g["ffn_bias2"], l1, p, SEED, synth.SITE_FFN_OUT)
+    l2, m2, r2 = ls.layernorm_fwd(f, g["gamma2"], g["beta2"], eps)
+    dx2, dg2, db2 = ls.layernorm_bwd(g["grad_y2"], f, g["gamma2"], m2, r2)
+    dx1, dg1, db1 = ls.layernorm_bwd(g["grad_y1"], a, g["gamma1"], m1, r1)
+    dprobs = ls.softmax_bwd(probs, g["grad_probs"])
+
+    k = shape.seq
+    o_probs = oracle.softmax_fwd(inp["scores"])
+    o_a = oracle.bias_dropout_residual(inp["attn_proj"], inp["attn_bias"], inp["residual"], p, SEED,
+                                       synth.SITE_ATTN_OUT, BITS)
+    o_l1, o_m1, o_r1 = oracle.layernorm_fwd(o_a, inp["gamma1"], inp["beta1"], eps)
+    o_act = oracle.bias_relu_dropout(inp["ffn_pre"], inp["ffn_bias1"], p, SEED, synth.SITE_FFN_ACT, BITS)
+    o_f = oracle.bias_dropout_residual(inp["ffn_proj"], inp["ffn_bias2"], o_l1, p, SEED, synth.SITE_FFN_OUT, BITS)
+    o_l2, o_m2, o_r2 = oracle.layernorm_fwd(o_f, inp["gamma2"], inp["beta2"], eps)
+    o_dx2, o_dg2, o_db2 = oracle.layernorm_bwd(inp["grad_y2"], o_f, inp["gamma2"], o_m2, o_r2)
+    o_dx1, o_dg1, o_db1 = oracle.layernorm_bwd(inp["grad_y1"], o_a, inp["gamma1"], o_m1, o_r1)
+    o_dprobs = oracle.softmax_bwd(o_probs.reshape(-1, k), inp["grad_probs"].reshape(-1, k)).reshape(o_probs.shape)
+
+    tag = f"chain config {config} ({shape.name})"
+    for name, got, ref in (("softmax fwd", probs, o_probs), ("attention bias+dropout+residual", a, o_a),
+                           ("LayerNorm 1", l1, o_l1), ("bias+ReLU+dropout", act, o_act),
+                           ("FFN bias+dropout+residual", f, o_f), ("LayerNorm 2", l2, o_l2),
+                           ("LayerNorm 2 dx", dx2, o_dx2), ("LayerNorm 2 dgamma", dg2, o_dg2),
+                           ("LayerNorm 2 dbeta", db2, o_db2), ("LayerNorm 1 dx", dx1, o_dx1),
+                           ("LayerNorm 1 dgamma", dg1, o_dg1), ("LayerNorm 1 dbeta", db1, o_db1),
+                           ("softmax bwd", dprobs, o_dprobs)):
+        assert_fp16(host(got), ref, f"{tag}: {name}")
+    chain_stats_bar(f"{tag}: LayerNorm 1", host(a), o_a, host(m1), host(r1), o_m1, o_r1)
+    chain_stats_bar(f"{tag}: LayerNorm 2", host(f), o_f, host(m2), host(r2), o_m2, o_r2)
+
+
+def chain_stats_bar(tag, x, o_x, mean, rstd, o_mean, o_rstd):
+    """LayerNorm statistics inside a chain.  Rows whose input is bit-identical
+    on both sides are held to the 1e-5 bar.  A row whose input differs (an
+    fp16 rounding upstream that went the other way, within the fp16 bar)
+    moves the statistics by the first-order change that difference causes:
+    d mean = sum(dx) / H, d rstd = -rstd^3 * sum((x - mean) * dx) / H; such
+    rows get the bar plus twice that change.  An fp32 result falls within
+    2^-24 of an fp16 rounding midpoint about once in 2^12 elements, so the
+    differing inputs must stay below 1e-3 of all elements."""
+    xg, xr = x.astype(np.float64), o_x.astype(np.float64)
+    differ = xg != xr
+    assert differ.mean() < 1e-3, f"{tag}: {int(differ.sum())} of {differ.size} inputs differ"
+    same = ~differ.any(axis=1)
+    om, ors = o_mean.astype(np.float64), o_rstd.astype(np.float64)
+    sigma = 1.0 / ors
+    assert_fp32(mean[same], o_mean[same], tag + " mean", floor=sigma[same])
+    assert_fp32(rstd[same], o_rstd[same], tag + " rstd")
+    if (~same).any():
+        d = (xg - xr)[~same]
+        h = x.shape[1]
+        d_mean = np.abs(d.sum(axis=1)) / h
+        d_rstd = ors[~same] ** 3 * np.abs(((xr[~same] - om[~same, None]) * d).sum(axis=1)) / h
+        gm, gr = mean[~same].astype(np.float64), rstd[~same].astype(np.float64)
+        assert (np.abs(gm - om[~same]) <= 1e-5 * np.maximum(np.abs(om[~same]), sigma[~same]) + 2 * d_mean).all(), \
+            tag + " mean (rows with differing input)"
+        assert (np.abs(gr - ors[~same]) <= 1e-5 * ors[~same] + 2 * d_rstd).all(), tag + " rstd (rows with differing input)"
+
+
 def test_graph_replay_matches_eager(ls):
     g = np.random.default_rng(77)
     T, H, F = 256, 768, 3072
