@@ -599,13 +599,14 @@ def write_chain_traffic(f_rows, w_rows, f_scale, w_scale, per_kernel):
     out = ["# HBM traffic per launch: BERT-base layer non-GEMM chain (4096 tokens, hidden 768, FFN 3072)", "",
            "Two `rocprofv3 --pmc` passes of `bench.py --eager` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), "
            f"scaled by what the same counters read for torch's 1 GiB device copy in the same runs (FETCH x{f_scale:.3f}, "
-           f"WRITE x{w_scale:.3f}). Commands, from the repository root on the GPU box (R = repository root):", "", "```",
-           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof_fetch "
+           f"WRITE x{w_scale:.3f}). Commands, from the repository root on the MI355X machine (R = repository root, "
+           "OUT = an output folder):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE -d $OUT/prof_fetch "
            "-o fetch --output-format csv -- python3 $R/bench.py --eager --steps 12 --warmup 2 --no-cpu --no-extra --no-info",
-           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof_write "
+           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE -d $OUT/prof_write "
            "-o write --output-format csv -- python3 $R/bench.py --eager --steps 12 --warmup 2 --no-cpu --no-extra --no-info",
-           "python bench.py --summarize-counters $R/gpurun_out/prof_fetch/fetch_counter_collection.csv "
-           "$R/gpurun_out/prof_write/write_counter_collection.csv", "```", "",
+           "python bench.py --summarize-counters $OUT/prof_fetch/fetch_counter_collection.csv "
+           "$OUT/prof_write/write_counter_collection.csv", "```", "",
            "| operator | kernel | dispatches | read MB | written MB | measured MB | algorithmic MB | measured / algorithmic |",
            "|---|---|---|---|---|---|---|---|"]
     for op, syms in CHAIN_SYMBOLS:
