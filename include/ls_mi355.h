@@ -321,15 +321,16 @@ int ls_probe_copy(void* dst, const void* src, int64_t bytes, void* stream);
 int ls_probe_read(float* sink, const void* src, int64_t bytes, void* stream);
 
 /* Kernel timing hook.  Arms two HIP events (hipEvent_t passed as void*) for
- * the calling thread: the next elementwise operator call
- * (ls_bias_dropout_residual, ls_bias_relu_dropout) launches its kernel with
- * hipExtLaunchKernel, which records start_event when the kernel begins and
- * stop_event when it ends, on the call's stream; then the events are
- * disarmed.  hipEventElapsedTime(start, stop) is then the kernel's own
- * duration, without the command processor's handling of separate event
- * records.  The library neither creates, waits on nor destroys the events.
- * Calls of other operators leave the armed events in place.  A NULL event
- * disarms and returns LS_ERR_NULL. */
+ * the calling thread: the next call of ls_bias_dropout_residual,
+ * ls_bias_relu_dropout or ls_layernorm_bwd (its row kernel, not the column
+ * sums after it) launches that kernel with hipExtLaunchKernel, which records
+ * start_event when the kernel begins and stop_event when it ends, on the
+ * call's stream; then the events are disarmed.  hipEventElapsedTime(start,
+ * stop) is then the kernel's own duration, without the command processor's
+ * handling of separate event records.  The library neither creates, waits
+ * on nor destroys the events.  Calls of other operators, and calls that
+ * return an error before launching, leave the armed events in place.  A NULL
+ * event disarms and returns LS_ERR_NULL. */
 int ls_time_next_launch(void* start_event, void* stop_event);
 
 /* Width in bits of the random field behind one dropout decision (16). */
