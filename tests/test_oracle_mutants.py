@@ -364,3 +364,44 @@ def test_pins_pass_on_the_oracle_itself():
             if (check, args) not in seen:
                 seen.add((check, args))
                 check(*args)
+
+
+# ------------------------------------------------ the dropout generator --
+
+import test_oracle_philox as philox_pins  # noqa: E402
+from oracle import philox  # noqa: E402
+from test_oracle_philox import rocrand_ref  # noqa: E402,F401  (the host build of rocRAND's engine, a fixture)
+
+_philox4x32 = philox.philox4x32
+
+
+def philox_nine_rounds(counter, key, rounds=10):
+    """Runs nine rounds instead of ten."""
+    return _philox4x32(counter, key, rounds - 1)
+
+
+def philox_swapped_multipliers(counter, key, rounds=10):
+    """Multiplies c0 by M1 and c2 by M0 (the round constants exchanged)."""
+    m = philox.MASK32
+    c0, c1, c2, c3 = np.broadcast_arrays(*(np.asarray(c, np.uint64) & m for c in counter))
+    k0, k1 = np.uint64(key[0] & 0xFFFFFFFF), np.uint64(key[1] & 0xFFFFFFFF)
+    for r in range(rounds):
+        if r > 0:
+            k0, k1 = (k0 + philox.PHILOX_W0) & m, (k1 + philox.PHILOX_W1) & m
+        p0, p1 = philox.PHILOX_M1 * c0, philox.PHILOX_M0 * c2
+        c0, c1, c2, c3 = (p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & m, (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & m
+    return c0, c1, c2, c3
+
+
+def philox_key_bumped_first(counter, key, rounds=10):
+    """Bumps the key before the first round as well."""
+    k = ((key[0] + 0x9E3779B9) & 0xFFFFFFFF, (key[1] + 0xBB67AE85) & 0xFFFFFFFF)
+    return _philox4x32(counter, k, rounds)
+
+
+@pytest.mark.parametrize("mutant", [philox_nine_rounds, philox_swapped_multipliers, philox_key_bumped_first],
+                         ids=lambda f: f.__name__)
+def test_philox_pins_catch_planted_mistake(monkeypatch, rocrand_ref, mutant):  # noqa: F811
+    monkeypatch.setattr(philox, "philox4x32", mutant)
+    with pytest.raises(AssertionError):
+        philox_pins.test_philox_matches_rocrand_engine(rocrand_ref, 0x0123456789ABCDEF, 3, 0)
