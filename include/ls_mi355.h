@@ -206,7 +206,7 @@ int ls_beam_topk(float* top_scores, int32_t* top_ids, const float* log_probs, co
  * y = (x - mean) * rstd * gamma + beta.
  * x, y: fp16 [rows, hidden]; gamma, beta: fp16 [hidden];
  * mean, rstd: fp32 [rows] (saved for the backward).  y may alias x.
- * eps > 0.  hidden must be in [1, 4096]. */
+ * eps > 0.  hidden must be in [1, 4096]; rows < 2^31 (else LS_ERR_SHAPE). */
 int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const void* gamma,
                      const void* beta, int64_t rows, int64_t hidden, float eps, void* stream);
 
@@ -225,6 +225,7 @@ size_t ls_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
  * [hidden]; mean, rstd: fp32 [rows] from ls_layernorm_fwd.  dx may alias dy.
  * workspace: device scratch of at least ls_layernorm_bwd_workspace_bytes()
  * bytes, 16-byte aligned; its contents on entry are ignored.
+ * rows < 2^31 (else LS_ERR_SHAPE).
  * Two kernel launches (row pass, then column finalisation). */
 int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
                      const void* gamma, const float* mean, const float* rstd, int64_t rows,
@@ -243,7 +244,7 @@ int ls_softmax_fwd(void* y, const void* x, int64_t batch, int64_t heads, int64_t
 
 /* Softmax backward from the stored output: dx = y * (dy - sum_j y_j dy_j)
  * per row.  y, dy, dx: fp16 [rows, k_len].  dx may alias dy.  Same k_len
- * limits as the forward. */
+ * limits as the forward; rows < 2^31 (else LS_ERR_SHAPE). */
 int ls_softmax_bwd(void* dx, const void* y, const void* dy, int64_t rows, int64_t k_len,
                    void* stream);
 

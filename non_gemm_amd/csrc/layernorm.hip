@@ -632,7 +632,7 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
     if (hidden == 0) return fail(LS_ERR_SHAPE, "%s: hidden must be >= 1", name);
     if (hidden > kMaxHidden)
         return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
-    if (rows >= (1ll << 32)) return fail(LS_ERR_SHAPE, "%s: too many rows", name);
+    if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", name);   // 32-bit row loops
     if (!y || !mean || !rstd || !x || !gamma || !beta) return fail(LS_ERR_NULL, "%s: null pointer", name);
     const bool vec = hidden % 8 == 0 && aligned16(y) && aligned16(x) && aligned16(gamma) && aligned16(beta);
     LnShape s;
@@ -672,7 +672,7 @@ int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const 
     if (hidden == 0) return fail(LS_ERR_SHAPE, "%s: hidden must be >= 1", name);
     if (hidden > kMaxHidden)
         return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
-    if (rows >= (1ll << 32)) return fail(LS_ERR_SHAPE, "%s: too many rows", name);
+    if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", name);   // 32-bit row loops
     if (!dx || !dgamma || !dbeta || !dy || !x || !gamma || !mean || !rstd || !workspace)
         return fail(LS_ERR_NULL, "%s: null pointer", name);
     const size_t need = ls_layernorm_bwd_workspace_bytes(rows, hidden);

@@ -518,7 +518,7 @@ int ls_softmax_bwd(void* dx, const void* y, const void* dy, int64_t rows, int64_
         set_dispatch("empty");
         return LS_OK;
     }
-    if (rows >= (1ll << 32)) return fail(LS_ERR_SHAPE, "%s: too many rows", name);
+    if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", name);   // 32-bit row loops
     if (!dx || !y || !dy) return fail(LS_ERR_NULL, "%s: null pointer", name);
     const bool vec = k_len % 8 == 0 && aligned16(dx) && aligned16(y) && aligned16(dy);
     SmShape s;

@@ -73,6 +73,10 @@ def test_layernorm_validation(lib):
     assert lib.ls_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8192, 1e-5, s) == LS_ERR_UNSUPPORTED
     assert lib.ls_layernorm_fwd(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 1e-5, s) == LS_ERR_NULL
     assert lib.ls_layernorm_fwd(None, None, None, None, None, None, 0, 8, 1e-5, s) == LS_OK
+    # 2^31 rows and more are refused before anything is launched (32-bit row loops)
+    assert lib.ls_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 31, 8, 1e-5, s) == LS_ERR_SHAPE
+    assert lib.ls_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 31, 8,
+                                FAKE, 1 << 40, s) == LS_ERR_SHAPE
     need = lib.ls_layernorm_bwd_workspace_bytes(4096, 768)
     assert need > 0 and need % (2 * 768 * 4) == 0
     assert lib.ls_layernorm_bwd_workspace_bytes(0, 768) == 0
@@ -95,6 +99,7 @@ def test_softmax_validation(lib):
     assert lib.ls_softmax_fwd(None, None, 0, 12, 128, 128, None, 1, s) == LS_OK
     assert lib.ls_softmax_bwd(FAKE, None, FAKE, 4, 128, s) == LS_ERR_NULL
     assert lib.ls_softmax_bwd(None, None, None, 0, 128, s) == LS_OK
+    assert lib.ls_softmax_bwd(FAKE, FAKE, FAKE, 1 << 31, 128, s) == LS_ERR_SHAPE      # 32-bit row loops
 
 
 def test_embedding_validation(lib):
