@@ -909,6 +909,89 @@ def test_graph_replay_matches_eager(ls):
         assert torch.allclose(got[-1], ref[-1], rtol=1e-5, atol=1e-4), f"replay {rep}: embedding gradient"
 
 
+def test_graph_replay_other_entry_points(ls):
+    """The remaining entry points captured in one HIP graph: every replay
+    (with eager work between replays) is bit-identical to the eager run.
+    Adam updates its buffers in place, so they are reset before each run."""
+    g = np.random.default_rng(78)
+    T, H, F, V = 256, 768, 3072, 4096
+    B, L, NH = 2, 128, 12
+    ids = dev(g.integers(0, 500, size=(B, L)).astype(np.int32))
+    E = dev(synth.normal16(g, (500, H), 0.02))
+    P = dev(synth.sinusoid_table(L, H))
+    dy = dev(synth.normal16(g, (T, H), 1.0))
+    dyf = dev(synth.normal16(g, (T, F), 1.0))
+    act = torch.relu(dev(synth.normal16(g, (T, F), 1.0)))
+    qkv = dev(synth.normal16(g, (T, 3 * H), 1.0))
+    qb = dev(synth.normal16(g, (3 * H,), 0.02))
+    dqo = dev(synth.normal16(g, (3, B, NH, L, H // NH), 1.0))
+    logits = dev(synth.normal16(g, (64, V), 2.0))
+    tgt = dev(g.integers(0, V, size=64).astype(np.int32))
+    lp = dev(g.normal(size=(4, 4, 2000)).astype(np.float32))
+    bs = dev(g.normal(size=(4, 4)).astype(np.float32))
+    p0 = dev(synth.normal16(g, (100_003,), 0.02))
+    gr = dev(synth.normal16(g, (100_003,), 1e-3))
+    m0 = torch.zeros(100_003, device="cuda")
+    f16 = dict(dtype=torch.float16, device="cuda")
+    o = {"emb": torch.empty((T, H), **f16), "dx1": torch.empty((T, H), **f16), "db1": torch.empty(H, **f16),
+         "dx2": torch.empty((T, F), **f16), "db2": torch.empty(F, **f16),
+         "qs": torch.empty((3, B, NH, L, H // NH), **f16), "dq": torch.empty((T, 3 * H), **f16),
+         "dqb": torch.empty(3 * H, **f16), "loss": torch.empty(64, device="cuda"),
+         "lse": torch.empty(64, device="cuda"), "dl": torch.empty((64, V), **f16),
+         "ts": torch.empty((4, 4), device="cuda"), "ti": torch.empty((4, 4), dtype=torch.int32, device="cuda"),
+         "p": torch.empty_like(p0), "m": torch.empty_like(m0), "v": torch.empty_like(m0)}
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    ws1 = torch.empty(max(ls.elementwise_bwd_workspace_bytes(T, H), 16), **u8)
+    ws2 = torch.empty(max(ls.elementwise_bwd_workspace_bytes(T, F), 16), **u8)
+    ws3 = torch.empty(max(ls.elementwise_bwd_workspace_bytes(T, 3 * H), 16), **u8)
+    from non_gemm_amd import _lib
+    ws4 = torch.empty(max(_lib.load().ls_beam_topk_workspace_bytes(4, 4, 4), 16), **u8)
+    hp = synth.ADAM_HYPER
+
+    def reset_adam():
+        o["p"].copy_(p0)
+        o["m"].copy_(m0)
+        o["v"].copy_(m0)
+
+    def step():
+        ls.embedding_fwd(ids, E, P, 27.7, 0.1, SEED, 3, out=o["emb"])
+        ls.bias_dropout_residual_bwd(dy, 0.1, SEED, 2, dx=o["dx1"], dbias=o["db1"], workspace=ws1)
+        ls.bias_relu_dropout_bwd(dyf, act, 0.1, dx=o["dx2"], dbias=o["db2"], workspace=ws2)
+        ls.bias_qkv_split(qkv, qb, B, L, NH, out=o["qs"])
+        ls.bias_qkv_split_bwd(dqo, dqkv=o["dq"], dbias=o["dqb"], workspace=ws3)
+        ls.cross_entropy_fwd(logits, tgt, 0.1, -1, loss=o["loss"], lse=o["lse"])
+        ls.cross_entropy_bwd(logits, tgt, o["lse"], 0.1, -1, 1.0 / 64, dlogits=o["dl"])
+        ls.beam_topk(lp, 4, bs, top_scores=o["ts"], top_ids=o["ti"], workspace=ws4)
+        ls.adam_workspace_step(o["p"], gr, o["m"], o["v"], hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                               hp["weight_decay"], 3, 1.0, True)
+
+    def snap():
+        torch.cuda.synchronize()
+        return {k: t.clone() for k, t in o.items()}
+
+    reset_adam()
+    step()
+    ref = snap()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    reset_adam()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    for rep in range(3):
+        for k, t in o.items():
+            t.fill_(3)                         # eager work between replays
+        reset_adam()
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snap()
+        for k in o:
+            assert torch.equal(got[k].view(torch.int16) if got[k].dtype == torch.float16 else got[k],
+                               ref[k].view(torch.int16) if ref[k].dtype == torch.float16 else ref[k]) or \
+                (got[k].dtype == torch.float32 and torch.equal(got[k].view(torch.int32), ref[k].view(torch.int32))), \
+                f"replay {rep}: {k} differs from the eager run"
+
+
 def test_timed_launch_same_result_and_events(ls):
     """ls_time_next_launch: the armed launch gives the same output, its events
     measure a positive duration, and the next call runs untimed."""
