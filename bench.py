@@ -531,6 +531,28 @@ def extra_rows(torch, ops):
     us_a = a.elapsed_time(b) / iters * 1e3
     out["adam_workspace_step"] = row("350M params, fp16 p/g, fp32 m/v, 1 launch", us_a, 22 * n,
                                      params_per_s=round(n / us_a * 1e6, 1))
+
+    # One GPU's share when the workspace is sharded 8 ways by range (43.75M
+    # parameters): the 8 ranges in turn, so no call finds its range in the caches.
+    n8 = n // 8
+    rngs = [slice(i * n8, (i + 1) * n8) for i in range(8)]
+
+    def adam_range(i):
+        r = rngs[i % 8]
+        ops.adam_workspace_step(prm[r], grd[r], m[r], v[r], hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                hp["weight_decay"], step[0], hp["grad_scale"], hp["decoupled_wd"])
+    for i in range(8):
+        adam_range(i)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record()
+    for i in range(5 * 8):
+        adam_range(i)
+    b.record()
+    torch.cuda.synchronize()
+    us_s = a.elapsed_time(b) / 40 * 1e3
+    out["adam_workspace_shard"] = row(f"{n8 / 1e6:.2f}M params (350M sharded 8 ways by range), 1 launch", us_s,
+                                      22 * n8, params_per_s=round(n8 / us_s * 1e6, 1))
     del prm, grd, m, v
     torch.cuda.empty_cache()
     return out
