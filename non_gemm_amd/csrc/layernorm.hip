@@ -25,13 +25,17 @@
 namespace ls {
 namespace {
 
-// Forward blocks: 1024 threads while a lane's raw row, gamma and beta fit
-// in at most ~48 registers (up to 4 16-byte chunks, or 16 elements on the
+// Forward blocks of 256 threads, or of 1024 when the rows give every CU a
+// whole 1024-thread block: fewer workgroups to dispatch for the same rows
+// (4096 x 768: 5.15 -> 4.70 us; 512 threads 5.01), but with fewer rows the
+// larger blocks leave CUs idle (1024 x 768: 3.61 us at 256 threads, 4.19 at
+// 1024).  The 1024-thread form exists while a lane's raw row, gamma and beta
+// fit in ~48 registers (up to 4 16-byte chunks, or 16 elements on the
 // element-wise path, which keeps one per register): at most ~105 VGPRs, no
-// spills.  Wider rows keep 256 (one wave per SIMD, all the registers).
-// Larger blocks mean fewer workgroups to dispatch for the same rows: 5.15 ->
-// 4.70 us at 4096 x 768 (512 threads: 5.01).
-constexpr int fwd_threads(int nch, int cw) { return (cw == 8 ? nch <= 4 : nch <= 16) ? 1024 : 256; }
+// spills.
+constexpr int kFwdSmall = 256;
+constexpr int kFwdBig = 1024;
+constexpr bool fwd_big_ok(int nch, int cw) { return cw == 8 ? nch <= 4 : nch <= 16; }
 
 template <int CW>
 struct Chunk;
@@ -100,13 +104,13 @@ struct Raw<1> {
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int LPR, int NCH, int CW>
-__global__ __launch_bounds__(fwd_threads(NCH, CW)) void ln_fwd_kernel(half_t* y, float* mean, float* rstd,
+template <int LPR, int NCH, int CW, int BT>
+__global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, float* rstd,
                                                         const half_t* x, const half_t* gamma,
                                                         const half_t* beta, uint32_t rows,
                                                         uint32_t h, float eps) {
     constexpr int RPW = kWave / LPR;
-    constexpr int kWaves = fwd_threads(NCH, CW) / kWave;
+    constexpr int kWaves = BT / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int l = lane % LPR;
@@ -548,10 +552,30 @@ bool ln_shape(int64_t h, bool vec, LnShape* s) {
 constexpr int64_t kMaxHidden = 4096;
 constexpr int kNumCU = 256;
 
-unsigned fwd_grid(int64_t rows, const LnShape& s) {
-    const int64_t per_block = fwd_threads(s.nch, s.cw) / kWave * (kWave / s.lpr);
+unsigned fwd_grid(int64_t rows, const LnShape& s, int threads) {
+    const int64_t per_block = threads / kWave * (kWave / s.lpr);
     const int64_t g = (rows + per_block - 1) / per_block;
     return static_cast<unsigned>(g < (1 << 20) ? g : (1 << 20));
+}
+
+// 1024-thread blocks when the shape allows them and the rows fill every CU
+// with one; 256 otherwise.
+int fwd_threads(int64_t rows, const LnShape& s) {
+    const bool ok = s.cw == 8 ? s.nch <= 4 : s.nch <= 16;
+    const int64_t rows_per_big = kFwdBig / kWave * (kWave / s.lpr);
+    return ok && rows >= kNumCU * rows_per_big ? kFwdBig : kFwdSmall;
+}
+
+template <int LPR, int NCH, int CW>
+void launch_ln_fwd(int threads, unsigned grid, hipStream_t st, half_t* y, float* mean, float* rstd,
+                   const half_t* x, const half_t* g, const half_t* b, uint32_t rows, uint32_t h, float eps) {
+    if constexpr (fwd_big_ok(NCH, CW)) {
+        if (threads == kFwdBig) {
+            ln_fwd_kernel<LPR, NCH, CW, kFwdBig><<<grid, kFwdBig, 0, st>>>(y, mean, rstd, x, g, b, rows, h, eps);
+            return;
+        }
+    }
+    ln_fwd_kernel<LPR, NCH, CW, kFwdSmall><<<grid, kFwdSmall, 0, st>>>(y, mean, rstd, x, g, b, rows, h, eps);
 }
 
 // Backward launch: waves per block (a power of two, 4 up to the shape's
@@ -580,8 +604,8 @@ BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
     return b;
 }
 
-#define LS_LN_FWD(LPR, NCH, CW)                                                                 \
-    ln_fwd_kernel<LPR, NCH, CW><<<grid, fwd_threads(NCH, CW), 0, st>>>(y16, mean, rstd, x16, g16, b16, r32, h32, eps)
+#define LS_LN_FWD(LPR, NCH, CW) \
+    launch_ln_fwd<LPR, NCH, CW>(threads, grid, st, y16, mean, rstd, x16, g16, b16, r32, h32, eps)
 #define LS_LN_BWD(LPR, NCH, CW)                                                                 \
     do {                                                                                        \
         if (bl.lds_bytes > 65536 &&                                                             \
@@ -637,7 +661,8 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
     const bool vec = hidden % 8 == 0 && aligned16(y) && aligned16(x) && aligned16(gamma) && aligned16(beta);
     LnShape s;
     ln_shape(hidden, vec, &s);
-    const unsigned grid = fwd_grid(rows, s);
+    const int threads = fwd_threads(rows, s);
+    const unsigned grid = fwd_grid(rows, s, threads);
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto* y16 = static_cast<half_t*>(y);
     auto* x16 = static_cast<const half_t*>(x);
@@ -647,7 +672,7 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
     clear_hip_error();
     LS_LN_TABLE(LS_LN_FWD)
     char buf[96];
-    snprintf(buf, sizeof(buf), "layernorm_fwd/%s", s.name);
+    snprintf(buf, sizeof(buf), "layernorm_fwd/%s_b%d", s.name, threads);
     set_dispatch(buf);
     return launch_status(name);
 }

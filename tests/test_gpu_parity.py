@@ -378,7 +378,7 @@ def test_beam_topk_ties_special_values_and_overflow(ls):
 
 LN_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (1000, 64), (77, 96), (33, 512), (9, 1536),
              (5, 2048), (3, 4096), (50, 100), (20, 13), (1, 8), (300, 768), (4, 4095),
-             (300, 2047), (64, 3001), (1030, 767)]
+             (300, 2047), (64, 3001), (1030, 767), (16384, 256), (4096, 1001)]
 
 
 def ln_inputs(rows, h, seed):
