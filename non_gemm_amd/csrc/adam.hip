@@ -1,9 +1,9 @@
 // Mixed-precision Adam over one contiguous fp16 workspace, one launch per
 // step ([L10] technique 3, slide 29; [LS2] sec. 2.3).
 //
-// Parameters and gradients live only in fp16; each lane widens 8 of them
-// (two 8-byte accesses each) to fp32 in registers, updates the fp32 moments
-// (two 16-byte accesses each), and writes the parameter back rounded to
+// Parameters and gradients live only in fp16; each lane widens 16 of them
+// (four 8-byte accesses each) to fp32 in registers, updates the fp32 moments
+// (four 16-byte accesses each), and writes the parameter back rounded to
 // fp16.  Per parameter: 12 bytes read, 10 written.  Because the whole model
 // sits in one workspace, the update is a single grid-stride kernel instead
 // of one small kernel per parameter tensor.
@@ -48,64 +48,62 @@ __global__ __launch_bounds__(kBlock) void adam_scalar_kernel(half_t* p, const ha
     }
 }
 
-// Vector body and scalar tail in one launch.  Each wave updates 512
-// consecutive parameters per iteration: lane L takes parameters 4L..4L+3 and
-// 256+4L..256+4L+3 of the span, so every load and store instruction of the
-// wave covers one contiguous run (512 bytes of fp16, 1 KiB of fp32).  (With
-// eight consecutive parameters per lane, each fp32 moment access was a
-// 32-byte-strided half of a 2 KiB run, twice the cache lines per
-// instruction: 1423 against 1375 us at 350M parameters.)  The last block
-// also finishes the parameters after the last whole group of four.
+// Vector body and scalar tail in one launch.  Each wave updates kSpan
+// consecutive parameters per iteration, in kGroups groups of 256: lane L
+// takes the four parameters at 4L of every group, so every load and store
+// instruction of the wave covers one contiguous run (512 bytes of fp16,
+// 1 KiB of fp32), and a lane has 4 x 4 loads in flight.  (Eight consecutive
+// parameters per lane made each fp32 moment access a 32-byte-strided half of
+// a 2 KiB run: 1423 us at 350M parameters; two groups per lane 1362 us, four
+// 1310 us, eight spill past the register budget.)  The last block also
+// finishes the parameters after the last whole group of four.
+constexpr int kGroups = 4;
+constexpr uint32_t kSpan = 256 * kGroups;                   // parameters per wave and iteration
+
 template <bool DECOUPLED>
 __global__ __launch_bounds__(kBlock) void adam_kernel(half_t* p, const half_t* g, float* m, float* v,
                                                       uint64_t n, uint64_t n4, AdamArgs a) {
-    constexpr uint32_t kSpan = 8 * kWave;                 // parameters per wave and iteration
     constexpr uint32_t kWavesPerBlock = kBlock / kWave;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint64_t grid_waves = static_cast<uint64_t>(gridDim.x) * kWavesPerBlock;
     for (uint64_t w = static_cast<uint64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; w * kSpan < n4;
          w += grid_waves) {
-        const uint64_t q0 = w * kSpan + 4 * lane, q1 = q0 + kSpan / 2;
-        const bool ok0 = q0 < n4, ok1 = q1 < n4;          // n4 % 4 == 0: a quad is whole or absent
         // Every byte is touched exactly once per step: non-temporal accesses
-        // stream it past the caches.
-        half4 p0{}, p1{}, g0{}, g1{};
-        float4v m0{}, m1{}, v0{}, v1{};
-        if (ok0) {
-            p0 = __builtin_nontemporal_load(reinterpret_cast<const half4*>(p + q0));
-            g0 = __builtin_nontemporal_load(reinterpret_cast<const half4*>(g + q0));
-            m0 = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(m + q0));
-            v0 = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(v + q0));
-        }
-        if (ok1) {
-            p1 = __builtin_nontemporal_load(reinterpret_cast<const half4*>(p + q1));
-            g1 = __builtin_nontemporal_load(reinterpret_cast<const half4*>(g + q1));
-            m1 = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(m + q1));
-            v1 = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(v + q1));
+        // stream it past the caches.  All loads before the first wait.
+        half4 pq[kGroups], gq[kGroups];
+        float4v mq[kGroups], vq[kGroups];
+        bool ok[kGroups];
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            const uint64_t i = w * kSpan + 256u * q + 4u * lane;
+            ok[q] = i < n4;                                 // n4 % 4 == 0: a group of four is whole or absent
+            pq[q] = gq[q] = half4{};
+            mq[q] = vq[q] = float4v{};
+            if (ok[q]) {
+                pq[q] = __builtin_nontemporal_load(reinterpret_cast<const half4*>(p + i));
+                gq[q] = __builtin_nontemporal_load(reinterpret_cast<const half4*>(g + i));
+                mq[q] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(m + i));
+                vq[q] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(v + i));
+            }
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float mk = m0[k], vk = v0[k];
-            p0[k] = static_cast<half_t>(adam_one<DECOUPLED>(static_cast<float>(p0[k]), static_cast<float>(g0[k]),
-                                                            mk, vk, a));
-            m0[k] = mk;
-            v0[k] = vk;
-            mk = m1[k];
-            vk = v1[k];
-            p1[k] = static_cast<half_t>(adam_one<DECOUPLED>(static_cast<float>(p1[k]), static_cast<float>(g1[k]),
-                                                            mk, vk, a));
-            m1[k] = mk;
-            v1[k] = vk;
-        }
-        if (ok0) {
-            __builtin_nontemporal_store(p0, reinterpret_cast<half4*>(p + q0));
-            __builtin_nontemporal_store(m0, reinterpret_cast<float4v*>(m + q0));
-            __builtin_nontemporal_store(v0, reinterpret_cast<float4v*>(v + q0));
-        }
-        if (ok1) {
-            __builtin_nontemporal_store(p1, reinterpret_cast<half4*>(p + q1));
-            __builtin_nontemporal_store(m1, reinterpret_cast<float4v*>(m + q1));
-            __builtin_nontemporal_store(v1, reinterpret_cast<float4v*>(v + q1));
+        for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float mk = mq[q][k], vk = vq[q][k];
+                pq[q][k] = static_cast<half_t>(adam_one<DECOUPLED>(static_cast<float>(pq[q][k]),
+                                                                   static_cast<float>(gq[q][k]), mk, vk, a));
+                mq[q][k] = mk;
+                vq[q][k] = vk;
+            }
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            const uint64_t i = w * kSpan + 256u * q + 4u * lane;
+            if (ok[q]) {
+                __builtin_nontemporal_store(pq[q], reinterpret_cast<half4*>(p + i));
+                __builtin_nontemporal_store(mq[q], reinterpret_cast<float4v*>(m + i));
+                __builtin_nontemporal_store(vq[q], reinterpret_cast<float4v*>(v + i));
+            }
         }
     }
     if (blockIdx.x == gridDim.x - 1) {
@@ -164,10 +162,10 @@ extern "C" int ls_adam_workspace_step(void* param, const void* grad, float* exp_
     clear_hip_error();
     if (vec) {
         const uint64_t n4 = un / 4 * 4;
-        // One block per span of 4 waves x 512 parameters: a capped
+        // One block per span of 4 waves x kSpan parameters: a capped
         // grid-stride launch measured slower on 256 CUs, whose block dispatch
         // keeps up with this body.
-        const uint64_t per_block = static_cast<uint64_t>(kBlock / kWave) * 8 * kWave;
+        const uint64_t per_block = static_cast<uint64_t>(kBlock / kWave) * kSpan;
         uint64_t blocks = (n4 + per_block - 1) / per_block;
         const uint64_t cap = 1ull << 30;
         if (blocks > cap) blocks = cap;
