@@ -325,7 +325,9 @@ int ls_beam_topk(float* top_scores, int32_t* top_ids, const float* log_probs, co
         static_cast<uint32_t>(k));
     int rc = launch_status(name);
     if (rc != LS_OK) return rc;
-    beam_merge_kernel<<<static_cast<unsigned>(batch), kMergeBlock, 0, st>>>(top_scores, top_ids, best,
+    // beam * k <= 64 winners are sorted by one wave in registers: a one-wave block.
+    const unsigned merge_threads = beam * k <= kWave ? kWave : kMergeBlock;
+    beam_merge_kernel<<<static_cast<unsigned>(batch), merge_threads, 0, st>>>(top_scores, top_ids, best,
                                                                           static_cast<uint32_t>(beam),
                                                                           static_cast<uint32_t>(k));
     set_dispatch("beam_topk/hars_rows_block1024_merge");
