@@ -253,7 +253,12 @@ def _rank_keys(c):
 
 
 def beam_candidates(log_probs, beam_scores):
-    """c[b, i, v] = log_probs[b, i, v] + beam_scores[b, i], one float32 add."""
+    """c[b, i, v] = log_probs[b, i, v] + beam_scores[b, i], one float32 add.
+
+    Parity: pinned by a hand-computed fixture (tests/golden/
+    beam_candidates_fp32.txt: exact sums, ties to even, an absorbed
+    addend) and by the full sort, whose candidates come from torch.
+    """
     lp = np.asarray(log_probs, np.float32)
     if beam_scores is None:
         return lp.copy()

@@ -27,3 +27,16 @@ def hars_example():
     beam, vocab = int(d["beam"]), int(d["vocab"])
     lp = np.stack([d[f"logits_beam{i}"] for i in range(beam)]).astype(np.float32).reshape(1, beam, vocab)
     return lp, int(d["k"]), int(d["candidates"]), int(d["survivors"])
+
+
+def beam_candidates_example():
+    """(log_probs float32 [1, beam, vocab], beam_scores float32 [1, beam],
+    hand-computed candidates float32 [1, beam, vocab], k, top ids, top scores)."""
+    d = load("beam_candidates_fp32.txt")
+    beam, vocab = int(d["beam"]), int(d["vocab"])
+    lp = np.stack([d[f"log_probs_beam{i}"] for i in range(beam)]).astype(np.float32).reshape(1, beam, vocab)
+    bs = np.asarray(d["beam_scores"], np.float32).reshape(1, beam)
+    c = np.stack([d[f"candidates_beam{i}"] for i in range(beam)]).astype(np.float32).reshape(1, beam, vocab)
+    ids = np.asarray(d["top_ids"]).astype(np.int32).reshape(1, -1)
+    scores = np.asarray(d["top_scores"], np.float32).reshape(1, -1)
+    return lp, bs, c, int(d["k"]), ids, scores

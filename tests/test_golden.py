@@ -4,7 +4,7 @@ import numpy as np
 
 import bench
 import oracle
-from golden_data import hars_example, load
+from golden_data import beam_candidates_example, hars_example, load
 
 
 def test_hars_worked_example_counts():
@@ -18,6 +18,19 @@ def test_hars_worked_example_counts():
     order = np.lexsort((np.arange(flat.size), -flat))[:k]       # value descending, then index
     np.testing.assert_array_equal(i[0], order)
     np.testing.assert_array_equal(s[0], lp.reshape(-1)[order])
+
+
+def test_beam_candidates_hand_computed():
+    """Candidates with beam scores: one float32 addition, rounded to nearest
+    even, worked out by hand in the fixture (exact sums, a tie to even in each
+    direction, an absorbed quarter spacing); the top two follow from them."""
+    lp, bs, c_ref, k, ids_ref, scores_ref = beam_candidates_example()
+    c = oracle.beam_candidates(lp, bs)
+    assert c.dtype == np.float32 and c.shape == c_ref.shape
+    np.testing.assert_array_equal(c.view(np.uint32), c_ref.view(np.uint32))
+    s, i = oracle.hars_topk(lp, bs, k)
+    np.testing.assert_array_equal(i, ids_ref)
+    np.testing.assert_array_equal(s.view(np.uint32), scores_ref.view(np.uint32))
 
 
 def test_fused_elementwise_traffic_matches_the_pages_count():

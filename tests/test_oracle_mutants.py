@@ -237,6 +237,22 @@ def hars_strict_threshold(log_probs, beam_scores, k, return_survivors=False):
     return (scores, ids, surv) if return_survivors else (scores, ids)
 
 
+def beam_candidates_sign_flipped(log_probs, beam_scores):
+    """Subtracts the beam score instead of adding it."""
+    lp = np.asarray(log_probs, np.float32)
+    if beam_scores is None:
+        return lp.copy()
+    return (lp - np.asarray(beam_scores, np.float32)[:, :, None]).astype(np.float32)
+
+
+def beam_candidates_unrounded(log_probs, beam_scores):
+    """Adds in float64 and keeps the sum unrounded."""
+    lp = np.asarray(log_probs, np.float64)
+    if beam_scores is None:
+        return lp.copy()
+    return lp + np.asarray(beam_scores, np.float64)[:, :, None]
+
+
 def bdr_bwd_no_mask(dy, p, seed, offset, bits):
     """Passes dy through without the dropout mask."""
     dy64 = np.asarray(dy, np.float64)
@@ -338,6 +354,9 @@ def _cases():
                                                             (pins.test_xent_invariants_and_bad_targets, ())]),
         ("cross_entropy_bwd", xent_bwd_no_smoothing_floor, [(pins.test_xent_matches_torch_and_logsumexp, (0.1,)),
                                                              (pins.test_xent_invariants_and_bad_targets, ())]),
+        ("beam_candidates", beam_candidates_sign_flipped, [(golden.test_beam_candidates_hand_computed, ()),
+                                                           (pins.test_hars_equals_full_sort, (3, 4, 50, 4))]),
+        ("beam_candidates", beam_candidates_unrounded, [(golden.test_beam_candidates_hand_computed, ())]),
         ("hars_topk", hars_strict_threshold, [(pins.test_hars_worked_example_keeps_5_of_16, ()),
                                               (golden.test_hars_worked_example_counts, ())]),
     ]
@@ -346,6 +365,7 @@ def _cases():
 @pytest.mark.parametrize("name,mutant,checks", _cases(), ids=lambda v: getattr(v, "__name__", None))
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant, checks):
     monkeypatch.setattr(oracle, name, mutant)
+    monkeypatch.setattr(oracle.ops, name, mutant)      # the oracle's own calls see it too
     failed = []
     for check, args in checks:
         try:

@@ -255,8 +255,13 @@ def test_xent_invariants_and_bad_targets():
 # ----------------------------------------------------------------------------
 
 def _full_sort_topk(lp, bs, k):
-    """Every candidate sorted: value descending (NaN first, -0 below +0), then index."""
-    c = oracle.beam_candidates(lp, bs)
+    """Every candidate sorted: value descending (NaN first, -0 below +0), then
+    index.  The candidates come from torch's float32 addition, not from the
+    oracle."""
+    c = torch.from_numpy(np.ascontiguousarray(lp, np.float32))
+    if bs is not None:
+        c = c + torch.from_numpy(np.ascontiguousarray(bs, np.float32))[:, :, None]
+    c = c.numpy()
     batch = c.shape[0]
     flat = c.reshape(batch, -1)
     out_s, out_i = [], []
