@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -54,7 +55,10 @@ LARGEST = "bias_relu_dropout"
 # Algorithmic (fused-minimum) byte counts
 # ---------------------------------------------------------------------------
 
-def chain_bytes(tokens, hidden, ffn, heads, seq):
+def chain_bytes(tokens, hidden, ffn, heads, seq, fused=True):
+    """Algorithmic bytes per call of every operator, calls per step, and the
+    step's total.  fused: each bias+dropout+residual and the LayerNorm after
+    it are one operator, which does not read its own sum back."""
     e_h, e_f = tokens * hidden, tokens * ffn
     e_s = (tokens // seq) * heads * seq * seq
     rows = tokens
@@ -62,13 +66,18 @@ def chain_bytes(tokens, hidden, ffn, heads, seq):
         "softmax_fwd": 4 * e_s,                                   # read x, write y
         "bias_dropout_residual": 6 * e_h + 2 * hidden,            # x, residual, out (+bias)
         "layernorm_fwd": 4 * e_h + 8 * rows + 4 * hidden,         # x, y, mean+rstd (+gamma, beta)
+        # x, residual, z, y, mean+rstd (+bias, gamma, beta)
+        "bias_dropout_residual_layernorm": 8 * e_h + 8 * rows + 6 * hidden,
         "bias_relu_dropout": 4 * e_f + 2 * ffn,                   # x, out (+bias)
         "layernorm_bwd": 6 * e_h + 8 * rows + 6 * hidden,         # dy, x, dx, stats, gamma, dgamma, dbeta
         "softmax_bwd": 6 * e_s,                                   # y, dy, dx
     }
-    counts = {"softmax_fwd": 1, "bias_dropout_residual": 2, "layernorm_fwd": 2, "bias_relu_dropout": 1,
-              "layernorm_bwd": 2, "softmax_bwd": 1}
-    total = sum(per[k] * counts[k] for k in per)
+    counts = {"softmax_fwd": 1, "bias_relu_dropout": 1, "layernorm_bwd": 2, "softmax_bwd": 1}
+    if fused:
+        counts["bias_dropout_residual_layernorm"] = 2
+    else:
+        counts.update(bias_dropout_residual=2, layernorm_fwd=2)
+    total = sum(per[k] * counts[k] for k in counts)
     return per, counts, total
 
 
@@ -139,7 +148,7 @@ class KernelEvents:
 class ChainSet:
     """Device buffers of one step, and its launches as (name, bytes, call)."""
 
-    def __init__(self, torch, inputs, shape, lib, per_bytes, p, seed, eps):
+    def __init__(self, torch, inputs, shape, lib, per_bytes, p, seed, eps, fused=True):
         d = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
         self.t = {k: d(v) for k, v in inputs.items()}
         t = self.t
@@ -169,19 +178,32 @@ class ChainSet:
         import synth
         pb = per_bytes
         # (name, algorithmic bytes, ctypes function, args)
+        if fused:
+            sub1 = [("bias_dropout_residual_layernorm", pb["bias_dropout_residual_layernorm"],
+                     lib.ls_bias_dropout_residual_layernorm,
+                     (P["attn_out"], P["ln1"], P["mean1"], P["rstd1"], P["attn_proj"], P["attn_bias"], P["residual"],
+                      P["gamma1"], P["beta1"], T, H, p, seed, synth.SITE_ATTN_OUT, eps, S))]
+            sub2 = [("bias_dropout_residual_layernorm", pb["bias_dropout_residual_layernorm"],
+                     lib.ls_bias_dropout_residual_layernorm,
+                     (P["ffn_out"], P["ln2"], P["mean2"], P["rstd2"], P["ffn_proj"], P["ffn_bias2"], P["ln1"],
+                      P["gamma2"], P["beta2"], T, H, p, seed, synth.SITE_FFN_OUT, eps, S))]
+        else:
+            sub1 = [("bias_dropout_residual", pb["bias_dropout_residual"], lib.ls_bias_dropout_residual,
+                     (P["attn_out"], P["attn_proj"], P["attn_bias"], P["residual"], T, H, p, seed,
+                      synth.SITE_ATTN_OUT, S)),
+                    ("layernorm_fwd", pb["layernorm_fwd"], lib.ls_layernorm_fwd,
+                     (P["ln1"], P["mean1"], P["rstd1"], P["attn_out"], P["gamma1"], P["beta1"], T, H, eps, S))]
+            sub2 = [("bias_dropout_residual", pb["bias_dropout_residual"], lib.ls_bias_dropout_residual,
+                     (P["ffn_out"], P["ffn_proj"], P["ffn_bias2"], P["ln1"], T, H, p, seed, synth.SITE_FFN_OUT, S)),
+                    ("layernorm_fwd", pb["layernorm_fwd"], lib.ls_layernorm_fwd,
+                     (P["ln2"], P["mean2"], P["rstd2"], P["ffn_out"], P["gamma2"], P["beta2"], T, H, eps, S))]
         self.launches = [
             ("softmax_fwd", pb["softmax_fwd"], lib.ls_softmax_fwd,
              (P["probs"], P["scores"], B, NH, L, L, None, 0, S)),
-            ("bias_dropout_residual", pb["bias_dropout_residual"], lib.ls_bias_dropout_residual,
-             (P["attn_out"], P["attn_proj"], P["attn_bias"], P["residual"], T, H, p, seed, synth.SITE_ATTN_OUT, S)),
-            ("layernorm_fwd", pb["layernorm_fwd"], lib.ls_layernorm_fwd,
-             (P["ln1"], P["mean1"], P["rstd1"], P["attn_out"], P["gamma1"], P["beta1"], T, H, eps, S)),
+            *sub1,
             ("bias_relu_dropout", pb["bias_relu_dropout"], lib.ls_bias_relu_dropout,
              (P["ffn_act"], P["ffn_pre"], P["ffn_bias1"], T, F, p, seed, synth.SITE_FFN_ACT, S)),
-            ("bias_dropout_residual", pb["bias_dropout_residual"], lib.ls_bias_dropout_residual,
-             (P["ffn_out"], P["ffn_proj"], P["ffn_bias2"], P["ln1"], T, H, p, seed, synth.SITE_FFN_OUT, S)),
-            ("layernorm_fwd", pb["layernorm_fwd"], lib.ls_layernorm_fwd,
-             (P["ln2"], P["mean2"], P["rstd2"], P["ffn_out"], P["gamma2"], P["beta2"], T, H, eps, S)),
+            *sub2,
             ("layernorm_bwd", pb["layernorm_bwd"], lib.ls_layernorm_bwd,
              (P["dx2"], P["dg2"], P["db2"], P["grad_y2"], P["ffn_out"], P["gamma2"], P["mean2"], P["rstd2"],
               T, H, P["ws2"], ws, S)),
@@ -198,11 +220,11 @@ class ChainSet:
                 check(name, fn(*args))
 
 
-def build_sets(torch, lib, shape, nsets, p, seed, eps, config=3):
+def build_sets(torch, lib, shape, nsets, p, seed, eps, config=3, fused=True):
     import synth
-    per, counts, total = chain_bytes(shape.tokens, shape.hidden, shape.ffn, shape.heads, shape.seq)
+    per, counts, total = chain_bytes(shape.tokens, shape.hidden, shape.ffn, shape.heads, shape.seq, fused)
     inputs = synth.chain_inputs(shape, config=config)
-    sets = [ChainSet(torch, inputs, shape, lib, per, p, seed, eps) for _ in range(nsets)]
+    sets = [ChainSet(torch, inputs, shape, lib, per, p, seed, eps, fused) for _ in range(nsets)]
     return sets, per, counts, total
 
 
@@ -222,11 +244,11 @@ def oracle_chain_pass(sl, shape, p, seed, eps):
     import oracle
     bits = 16
     probs = oracle.softmax_fwd(sl["scores"])
-    a = oracle.bias_dropout_residual(sl["attn_proj"], sl["attn_bias"], sl["residual"], p, seed, 0, bits)
-    l1, m1, r1 = oracle.layernorm_fwd(a, sl["gamma1"], sl["beta1"], eps)
+    a, l1, m1, r1 = oracle.bias_dropout_residual_layernorm(sl["attn_proj"], sl["attn_bias"], sl["residual"],
+                                                           sl["gamma1"], sl["beta1"], p, seed, 0, bits, eps)
     oracle.bias_relu_dropout(sl["ffn_pre"], sl["ffn_bias1"], p, seed, 1, bits)
-    f = oracle.bias_dropout_residual(sl["ffn_proj"], sl["ffn_bias2"], l1, p, seed, 2, bits)
-    l2, m2, r2 = oracle.layernorm_fwd(f, sl["gamma2"], sl["beta2"], eps)
+    f, l2, m2, r2 = oracle.bias_dropout_residual_layernorm(sl["ffn_proj"], sl["ffn_bias2"], l1, sl["gamma2"],
+                                                           sl["beta2"], p, seed, 2, bits, eps)
     oracle.layernorm_bwd(sl["grad_y2"], f, sl["gamma2"], m2, r2)
     oracle.layernorm_bwd(sl["grad_y1"], a, sl["gamma1"], m1, r1)
     k = shape.seq
@@ -407,12 +429,19 @@ def extra_rows(torch, ops):
     c4_row("bias_dropout_residual", [lambda s=s: ops.bias_dropout_residual(s[0], s[1], s[2], p, seed, 0, out=s[3])
                                      for s in bs])
     del bs
+    R = sets_for(per4["bias_dropout_residual_layernorm"])
+    gm, bt = rnd(H4_).abs() + 0.5, rnd(H4_)
+    bs = [(rnd(T4_, H4_), rnd(H4_), rnd(T4_, H4_), emp(T4_, H4_), emp(T4_, H4_), emp(T4_, dt=torch.float32),
+           emp(T4_, dt=torch.float32)) for _ in range(R)]
+    c4_row("bias_dropout_residual_layernorm",
+           [lambda s=s: ops.bias_dropout_residual_layernorm(s[0], s[1], s[2], gm, bt, p, seed, 0, synth.LN_EPS,
+                                                            z=s[3], y=s[4], mean=s[5], rstd=s[6]) for s in bs])
+    del bs
     R = sets_for(per4["bias_relu_dropout"])
     bs = [(rnd(T4_, F4_), rnd(F4_), emp(T4_, F4_)) for _ in range(R)]
     c4_row("bias_relu_dropout", [lambda s=s: ops.bias_relu_dropout(s[0], s[1], p, seed, 1, out=s[2]) for s in bs])
     del bs
     R = sets_for(per4["layernorm_fwd"])
-    gm, bt = rnd(H4_).abs() + 0.5, rnd(H4_)
     bs = [(rnd(T4_, H4_), emp(T4_, H4_), emp(T4_, dt=torch.float32), emp(T4_, dt=torch.float32)) for _ in range(R)]
     c4_row("layernorm_fwd", [lambda s=s: ops.layernorm_fwd(s[0], gm, bt, synth.LN_EPS, y=s[1], mean=s[2], rstd=s[3])
                              for s in bs])
@@ -603,11 +632,13 @@ def summarize_counters(fetch_csv, write_csv):
         write_chain_traffic(f_rows, w_rows, f_scale, w_scale, per_kernel)
 
 
-# Kernel symbols of each chain operator (substrings of the mangled names).
+# Kernel symbols of each chain operator (regular expressions over the mangled
+# names; the LayerNorm forward's last template argument is the fused flag).
 CHAIN_SYMBOLS = (
     ("softmax_fwd", ("softmax_fwd_kernel",)),
+    ("bias_dropout_residual_layernorm", (r"ln_fwd_kernel\w*Lb1EE",)),
     ("bias_dropout_residual", ("elementwise_vec_kernelILb1ELb0ELb1E",)),       # RESID=1, RELU=0, DROP=1
-    ("layernorm_fwd", ("ln_fwd_kernel",)),
+    ("layernorm_fwd", (r"ln_fwd_kernel\w*Lb0EE",)),
     ("bias_relu_dropout", ("elementwise_vec_kernelILb0ELb1ELb1E",)),
     ("layernorm_bwd", ("ln_bwd_kernel", "ln_bwd_finalize_kernel")),
     ("softmax_bwd", ("softmax_bwd_kernel",)),
@@ -632,16 +663,18 @@ def write_chain_traffic(f_rows, w_rows, f_scale, w_scale, per_kernel):
            "| operator | kernel | dispatches | read MB | written MB | measured MB | algorithmic MB | measured / algorithmic |",
            "|---|---|---|---|---|---|---|---|"]
     for op, syms in CHAIN_SYMBOLS:
-        tot = 0.0
+        tot, seen = 0.0, False
         for sym in syms:
-            f, nf = per_kernel(f_rows, lambda k, s=sym: s in k)
-            w, _ = per_kernel(w_rows, lambda k, s=sym: s in k)
+            f, nf = per_kernel(f_rows, lambda k, s=sym: re.search(s, k) is not None)
+            w, _ = per_kernel(w_rows, lambda k, s=sym: re.search(s, k) is not None)
             if f is None or w is None:
                 continue
             rd, wr = f * 1024 * f_scale / 1e6, w * 1024 * w_scale / 1e6
             tot += rd + wr
+            seen = True
             out.append(f"| {op} | `{sym}` | {nf} | {rd:.2f} | {wr:.2f} | {rd + wr:.2f} | | |")
-        out.append(f"| **{op}** | all | | | | **{tot:.2f}** | {per[op] / 1e6:.2f} | **{tot * 1e6 / per[op]:.3f}** |")
+        if seen:
+            out.append(f"| **{op}** | all | | | | **{tot:.2f}** | {per[op] / 1e6:.2f} | **{tot * 1e6 / per[op]:.3f}** |")
     path = os.path.join(ROOT, "profiles", "chain_bert_base_4096tok_traffic.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
@@ -759,6 +792,40 @@ def attainable(torch, lib, check, cap_stream, dom_bytes):
     out["copy_dominant_bytes_GBps"], out["copy_dominant_bytes_us"] = rate(pairs, lib.ls_probe_copy, 2 * half)
     out["copy_dominant_bytes"] = 2 * half
     del pairs
+    torch.cuda.empty_cache()
+    return out
+
+
+def unfused_chain(torch, lib, check, cap_stream, p, seed, eps, nsets=12, reps=20):
+    """The same BERT-base step with bias+dropout+residual and LayerNorm as two
+    operators each (11 calls per step), on its own rotated sets: the
+    comparison point for the fused step."""
+    import synth
+    shape = synth.C3
+    sets, per, counts, total = build_sets(torch, lib, shape, nsets, p, seed, eps, fused=False)
+    for s in sets:
+        s.run(check)
+    graphs = []
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            st = torch.cuda.current_stream().cuda_stream
+            for nm, _, fn, a in s.launches:
+                check(nm, fn(*a[:-1], st))
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(graphs))
+    out = {"calls_per_step": len(sets[0].launches), "us_per_step": round(us, 2), "bytes_per_step": total,
+           "GB/s": round(total / us / 1e3, 1), "tokens_per_s": round(shape.tokens / (us * 1e-6), 1)}
+    del graphs, sets
     torch.cuda.empty_cache()
     return out
 
@@ -904,7 +971,7 @@ def main():
     # Informational: per-kernel cold times (graphs of R launches of one kind) and
     # the warm (single buffer set) chain.
     kernels = {}
-    for name in ([] if args.no_info else per):
+    for name in ([] if args.no_info else counts):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap_stream):
             st = torch.cuda.current_stream().cuda_stream
@@ -942,6 +1009,7 @@ def main():
     torch.cuda.synchronize()
     del graphs, sets
     torch.cuda.empty_cache()
+    unfused = None if args.no_info else unfused_chain(torch, lib, check, cap_stream, p, seed, eps, nsets=args.sets)
     reach = None if args.no_info else attainable(torch, lib, check, cap_stream, per[DOMINANT])
     big = None if args.no_info else transformer_big_chain(torch, lib, check, cap_stream, p, seed, eps)
 
@@ -968,7 +1036,9 @@ def main():
         "config": {"workload": "bert-base-layer-non-gemm-chain", "tokens": shape.tokens, "batch": shape.batch,
                    "seq_len": shape.seq, "hidden": shape.hidden, "heads": shape.heads, "ffn": shape.ffn,
                    "dropout_p": p, "chain_bytes_per_step": total, "rotated_sets": args.sets,
-                   "footprint_bytes": footprint, "launches_per_step": 11},
+                   "footprint_bytes": footprint, "launches_per_step": n_launch,
+                   "kernels_per_step": n_launch + counts["layernorm_bwd"],
+                   "fused_bias_dropout_residual_layernorm": True},
         "roofline": {"bound": "hbm", "kernel": f"{DOMINANT} row kernel {DOMINANT_SHAPE}",
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -980,6 +1050,7 @@ def main():
         "warm_chain_us": None if warm_us is None else round(warm_us, 2),
         "attainable_hbm": reach,
         "dispatch": dispatch,
+        "unfused_chain": unfused,
         "transformer_big_chain": big,
         "other_rows": extra,
         "wall_s_timed": round(wall, 4),

@@ -201,14 +201,38 @@ int ls_beam_topk(float* top_scores, int32_t* top_ids, const float* log_probs, co
                  size_t workspace_bytes, void* stream);
 
 /* LayerNorm forward with one fused reduction pass ([L10] technique 2,
- * slide 21): per row, S1 = sum x and S2 = sum x^2 are reduced together;
- * mean = S1/H, var = max(S2/H - mean^2, 0), rstd = 1/sqrt(var + eps),
- * y = (x - mean) * rstd * gamma + beta.
+ * slide 21): per row, with d = x - K and K the row's first element,
+ * S1 = sum d and S2 = sum d^2 are reduced together; mean = K + S1/H,
+ * var = max(S2/H - (S1/H)^2, 0), rstd = 1/sqrt(var + eps),
+ * y = (x - mean) * rstd * gamma + beta.  (The shift K leaves the one-pass
+ * formula exact in real arithmetic and keeps the fp32 statistics accurate
+ * on rows whose |mean| is large next to their spread.)
  * x, y: fp16 [rows, hidden]; gamma, beta: fp16 [hidden];
  * mean, rstd: fp32 [rows] (saved for the backward).  y may alias x.
- * eps > 0.  hidden must be in [1, 4096]; rows < 2^31 (else LS_ERR_SHAPE). */
+ * eps > 0.  hidden must be in [1, 4096]; rows < 2^31 (else LS_ERR_SHAPE).
+ * rows == 0 launches nothing. */
 int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const void* gamma,
                      const void* beta, int64_t rows, int64_t hidden, float eps, void* stream);
+
+/* Bias + dropout + residual followed by LayerNorm, in one launch: the
+ * sub-layer output block of a post-LN Transformer layer ([LS2] sec. 2.1.1;
+ * [L10] technique 1 fuses neighbouring memory-bound operators).
+ *     z = residual + Dropout(x + bias)      (exactly ls_bias_dropout_residual)
+ *     (y, mean, rstd) = LayerNorm(z)        (exactly ls_layernorm_fwd of z)
+ * z is rounded to fp16 and stored (the LayerNorm backward reads it), and the
+ * statistics are those of the stored z, so the outputs are bit-identical to
+ * the two calls one after the other; z is not read back from memory.
+ * x, residual, z, y: fp16 [rows, hidden]; bias, gamma, beta: fp16 [hidden];
+ * mean, rstd: fp32 [rows].  Dropout as in ls_bias_dropout_residual (flat
+ * element index row * hidden + col, site `offset`).  z may alias x or
+ * residual; y must not alias any input.
+ * p in [0, 1], eps > 0, hidden in [1, 4096], rows < 2^31.
+ * Errors: LS_ERR_SHAPE, LS_ERR_PARAM, LS_ERR_UNSUPPORTED (hidden > 4096),
+ * LS_ERR_NULL.  rows == 0 launches nothing. */
+int ls_bias_dropout_residual_layernorm(void* z, void* y, float* mean, float* rstd, const void* x,
+                                       const void* bias, const void* residual, const void* gamma,
+                                       const void* beta, int64_t rows, int64_t hidden, float p, uint64_t seed,
+                                       uint64_t offset, float eps, void* stream);
 
 /* Bytes of device scratch that ls_layernorm_bwd needs for this shape
  * (per-block fp32 column partials of dgamma and dbeta).  Depends only on

@@ -43,6 +43,9 @@ SIGNATURES = {
                              c_size, c_void_p]),
     "ls_layernorm_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_i64, c_i64, c_f32, c_void_p]),
+    "ls_bias_dropout_residual_layernorm": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                   c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_f32, c_u64,
+                                                   c_u64, c_f32, c_void_p]),
     "ls_layernorm_bwd_workspace_bytes": (c_size, [c_i64, c_i64]),
     "ls_layernorm_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_size, c_void_p]),

@@ -1,9 +1,10 @@
 // LayerNorm forward and backward ([L10] technique 2, slides 21-22).
 //
-// Forward: one fused reduction per row.  Each lane accumulates S1 = sum x
-// and S2 = sum x^2 over its elements; the two sums travel through the same
-// DPP/swizzle reduction, so the row needs a single cross-lane pass instead
-// of "mean first, then variance":  var = S2/H - (S1/H)^2 (clamped at 0).
+// Forward: one fused reduction per row.  Each lane accumulates S1 = sum d
+// and S2 = sum d^2 over its elements, d = x - K with K the row's first
+// element; the two sums travel through the same DPP/swizzle reduction, so
+// the row needs a single cross-lane pass instead of "mean first, then
+// variance":  mean = K + S1/H, var = S2/H - (S1/H)^2 (clamped at 0).
 //
 // Backward: the two row sums A = sum gamma*dy and B = sum gamma*dy*xhat are
 // likewise reduced together, then dx = rstd * (gamma*dy - A/H - xhat*B/H).
@@ -35,7 +36,10 @@ namespace {
 // spills.
 constexpr int kFwdSmall = 256;
 constexpr int kFwdBig = 1024;
-constexpr bool fwd_big_ok(int nch, int cw) { return cw == 8 ? nch <= 4 : nch <= 16; }
+constexpr bool fwd_big_ok(int nch, int cw, bool fused) {
+    // the fused form also holds the residual and bias chunks
+    return fused ? (cw == 8 ? nch <= 2 : nch <= 8) : (cw == 8 ? nch <= 4 : nch <= 16);
+}
 
 template <int CW>
 struct Chunk;
@@ -104,11 +108,24 @@ struct Raw<1> {
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int LPR, int NCH, int CW, int BT>
+// The fused form's extra operands: the row to normalise is
+// z = residual + keep * (x + bias) * scale, computed like the standalone
+// bias+dropout+residual (one fma per element, so z is bit-identical to it),
+// rounded to fp16 and stored (the backward reads it), and the stored value
+// is what the statistics see.  z may alias x or residual: each lane reads
+// its elements before it writes them.
+struct FwdFuse {
+    half_t* z;
+    const half_t* bias;
+    const half_t* residual;
+    Dropout d;
+};
+
+template <int LPR, int NCH, int CW, int BT, bool FUSED>
 __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, float* rstd,
                                                         const half_t* x, const half_t* gamma,
                                                         const half_t* beta, uint32_t rows,
-                                                        uint32_t h, float eps) {
+                                                        uint32_t h, float eps, FwdFuse fz) {
     constexpr int RPW = kWave / LPR;
     constexpr int kWaves = BT / kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -124,7 +141,8 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
         const size_t base = static_cast<size_t>(row) * h;
         // The row's chunks first, then gamma and beta (cache hits after the
         // first waves); one wait covers all of them.
-        typename R::T xr[NCH], gr[NCH], br[NCH];
+        constexpr int NF = FUSED ? NCH : 1;
+        typename R::T xr[NCH], gr[NCH], br[NCH], rr[NF], cr[NF];    // rr, cr: residual, bias
         if constexpr (CW == 1) {
             // Element-wise path: unconditional loads at indices clamped into
             // the tensor, out-of-range values zeroed afterwards (a load
@@ -136,6 +154,10 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
                 const uint32_t c = l + j * LPR;
                 const uint32_t cc = c < h ? c : h - 1;
                 xr[j] = R::load_cached(x, cbase + cc);
+                if constexpr (FUSED) {
+                    rr[j] = R::load_cached(fz.residual, cbase + cc);
+                    cr[j] = R::load_cached(fz.bias, cc);
+                }
                 gr[j] = R::load_cached(gamma, cc);
                 br[j] = R::load_cached(beta, cc);
             }
@@ -143,6 +165,10 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
             for (int j = 0; j < NCH; ++j) {
                 const bool in = ok && l + j * LPR < h;
                 xr[j] = in ? xr[j] : R::zero();
+                if constexpr (FUSED) {
+                    rr[j] = in ? rr[j] : R::zero();
+                    cr[j] = in ? cr[j] : R::zero();
+                }
                 gr[j] = in ? gr[j] : R::zero();
                 br[j] = in ? br[j] : R::zero();
             }
@@ -150,37 +176,90 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
 #pragma unroll
             for (int j = 0; j < NCH; ++j) xr[j] = gr[j] = br[j] = R::zero();
 #pragma unroll
+            for (int j = 0; j < NF; ++j) rr[j] = cr[j] = R::zero();
+#pragma unroll
             for (int j = 0; j < NCH; ++j) {
                 const uint32_t c = (l + j * LPR) * CW;
-                if (ok && c < h) xr[j] = R::load_cached(x, base + c);
+                if (ok && c < h) {
+                    if constexpr (FUSED) {
+                        // the fused inputs are read once: streamed
+                        xr[j] = R::load(x, base + c);
+                        rr[j] = R::load(fz.residual, base + c);
+                    } else {
+                        xr[j] = R::load_cached(x, base + c);
+                    }
+                }
             }
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
                 const uint32_t c = (l + j * LPR) * CW;
                 if (ok && c < h) {
+                    if constexpr (FUSED) cr[j] = R::load_cached(fz.bias, c);
                     gr[j] = R::load_cached(gamma, c);
                     br[j] = R::load_cached(beta, c);
                 }
             }
         }
         float v[NCH][CW];
+        if constexpr (FUSED) {
+            // z = residual + keep * (x + bias) * scale, rounded to fp16 and
+            // stored; the statistics and y use the stored value.
+            const bool drop = fz.d.thr != 0;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) R::widen(xr[j], v[j]);
+            for (int j = 0; j < NCH; ++j) {
+                const uint32_t c = (l + j * LPR) * CW;
+                float a[CW], b[CW], r[CW], f[CW], o[CW];
+                R::widen(xr[j], a);
+                R::widen(cr[j], b);
+                R::widen(rr[j], r);
+                const uint64_t i0 = static_cast<uint64_t>(row) * h + c;    // flat index of the chunk
+                if constexpr (CW == 8) {
+                    if (drop) dropout_factors8(fz.d, i0 >> 3, f);          // h % 8 == 0: one Philox call
+                    else
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) f[k] = 1.0f;
+                } else {
+                    f[0] = drop ? dropout_factor1(fz.d, i0) : 1.0f;
+                }
+#pragma unroll
+                for (int k = 0; k < CW; ++k) o[k] = fmaf(f[k], a[k] + b[k], r[k]);
+                if constexpr (CW == 8) {
+                    const half8 zh = pack8(o);
+                    if (ok && c < h) __builtin_nontemporal_store(zh, reinterpret_cast<half8*>(fz.z + base + c));
+                    unpack8(zh, v[j]);
+                } else {
+                    const half_t zh = static_cast<half_t>(o[0]);
+                    if (ok && c < h) fz.z[base + c] = zh;
+                    v[j][0] = static_cast<float>(zh);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) R::widen(xr[j], v[j]);
+        }
+        // The sums run over d = x - K with K the row's first element (held by
+        // the group's first lane): mean = K + S1'/H, var = S2'/H - (S1'/H)^2.
+        // Still one fused reduction, but the cancellation is between terms of
+        // the size of the row's spread rather than of its mean (shifted data,
+        // Chan, Golub & LeVeque 1983), so rows whose |mean| is large next to
+        // their spread keep fp32 accuracy.
+        const float K = group_first<LPR>(v[0][0], lane);
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
 #pragma unroll
             for (int k = 0; k < CW; ++k) {
+                v[j][k] -= K;
                 s1 += v[j][k];
                 s2 = fmaf(v[j][k], v[j][k], s2);
             }
-        s1 = group_sum<LPR>(s1);          // the one fused reduction: (S1, S2) together
+        s1 = group_sum<LPR>(s1);          // the one fused reduction: (S1', S2') together
         s2 = group_sum<LPR>(s2);
-        const float mu = s1 / hf;
-        const float var = fmaxf(s2 / hf - mu * mu, 0.0f);
+        const float md = s1 / hf;
+        const float var = fmaxf(s2 / hf - md * md, 0.0f);
         const float rs = rsqrtf(var + eps);
         if (ok && l == 0) {
-            mean[row] = mu;
+            mean[row] = K + md;
             rstd[row] = rs;
         }
 #pragma unroll
@@ -192,7 +271,7 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
                 R::widen(gr[j], g);
                 R::widen(br[j], b);
 #pragma unroll
-                for (int k = 0; k < CW; ++k) o[k] = fmaf((v[j][k] - mu) * rs, g[k], b[k]);
+                for (int k = 0; k < CW; ++k) o[k] = fmaf((v[j][k] - md) * rs, g[k], b[k]);
                 Chunk<CW>::store(y, base + c, o);
             }
         }
@@ -560,22 +639,24 @@ unsigned fwd_grid(int64_t rows, const LnShape& s, int threads) {
 
 // 1024-thread blocks when the shape allows them and the rows fill every CU
 // with one; 256 otherwise.
-int fwd_threads(int64_t rows, const LnShape& s) {
-    const bool ok = s.cw == 8 ? s.nch <= 4 : s.nch <= 16;
+int fwd_threads(int64_t rows, const LnShape& s, bool fused) {
     const int64_t rows_per_big = kFwdBig / kWave * (kWave / s.lpr);
-    return ok && rows >= kNumCU * rows_per_big ? kFwdBig : kFwdSmall;
+    return fwd_big_ok(s.nch, s.cw, fused) && rows >= kNumCU * rows_per_big ? kFwdBig : kFwdSmall;
 }
 
-template <int LPR, int NCH, int CW>
+template <int LPR, int NCH, int CW, bool FUSED>
 void launch_ln_fwd(int threads, unsigned grid, hipStream_t st, half_t* y, float* mean, float* rstd,
-                   const half_t* x, const half_t* g, const half_t* b, uint32_t rows, uint32_t h, float eps) {
-    if constexpr (fwd_big_ok(NCH, CW)) {
+                   const half_t* x, const half_t* g, const half_t* b, uint32_t rows, uint32_t h, float eps,
+                   const FwdFuse& fz) {
+    if constexpr (fwd_big_ok(NCH, CW, FUSED)) {
         if (threads == kFwdBig) {
-            ln_fwd_kernel<LPR, NCH, CW, kFwdBig><<<grid, kFwdBig, 0, st>>>(y, mean, rstd, x, g, b, rows, h, eps);
+            launch_kernel(ln_fwd_kernel<LPR, NCH, CW, kFwdBig, FUSED>, dim3(grid), dim3(kFwdBig), 0, st, y, mean,
+                          rstd, x, g, b, rows, h, eps, fz);
             return;
         }
     }
-    ln_fwd_kernel<LPR, NCH, CW, kFwdSmall><<<grid, kFwdSmall, 0, st>>>(y, mean, rstd, x, g, b, rows, h, eps);
+    launch_kernel(ln_fwd_kernel<LPR, NCH, CW, kFwdSmall, FUSED>, dim3(grid), dim3(kFwdSmall), 0, st, y, mean, rstd,
+                  x, g, b, rows, h, eps, fz);
 }
 
 // Backward launch: waves per block (a power of two, 4 up to the shape's
@@ -605,7 +686,9 @@ BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
 }
 
 #define LS_LN_FWD(LPR, NCH, CW) \
-    launch_ln_fwd<LPR, NCH, CW>(threads, grid, st, y16, mean, rstd, x16, g16, b16, r32, h32, eps)
+    launch_ln_fwd<LPR, NCH, CW, false>(threads, grid, st, y16, mean, rstd, x16, g16, b16, r32, h32, eps, fz)
+#define LS_LN_FWD_FUSED(LPR, NCH, CW) \
+    launch_ln_fwd<LPR, NCH, CW, true>(threads, grid, st, y16, mean, rstd, x16, g16, b16, r32, h32, eps, fz)
 #define LS_LN_BWD(LPR, NCH, CW)                                                                 \
     do {                                                                                        \
         if (bl.lds_bytes > 65536 &&                                                             \
@@ -661,7 +744,7 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
     const bool vec = hidden % 8 == 0 && aligned16(y) && aligned16(x) && aligned16(gamma) && aligned16(beta);
     LnShape s;
     ln_shape(hidden, vec, &s);
-    const int threads = fwd_threads(rows, s);
+    const int threads = fwd_threads(rows, s, false);
     const unsigned grid = fwd_grid(rows, s, threads);
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto* y16 = static_cast<half_t*>(y);
@@ -669,10 +752,55 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
     auto* g16 = static_cast<const half_t*>(gamma);
     auto* b16 = static_cast<const half_t*>(beta);
     const uint32_t r32 = static_cast<uint32_t>(rows), h32 = static_cast<uint32_t>(hidden);
+    const FwdFuse fz{};
     clear_hip_error();
     LS_LN_TABLE(LS_LN_FWD)
     char buf[96];
     snprintf(buf, sizeof(buf), "layernorm_fwd/%s_b%d", s.name, threads);
+    set_dispatch(buf);
+    return launch_status(name);
+}
+
+int ls_bias_dropout_residual_layernorm(void* z, void* y, float* mean, float* rstd, const void* x,
+                                       const void* bias, const void* residual, const void* gamma,
+                                       const void* beta, int64_t rows, int64_t hidden, float p, uint64_t seed,
+                                       uint64_t offset, float eps, void* stream) {
+    using namespace ls;
+    const char* name = "ls_bias_dropout_residual_layernorm";
+    if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    if (!(eps > 0.0f) || !host_finite(eps)) return fail(LS_ERR_PARAM, "%s: eps must be > 0", name);
+    FwdFuse fz;
+    if (!make_dropout(p, seed, offset, &fz.d))
+        return fail(LS_ERR_PARAM, "%s: dropout probability %g outside [0, 1]", name, (double)p);
+    if (rows == 0) {
+        set_dispatch("empty");
+        return LS_OK;
+    }
+    if (hidden == 0) return fail(LS_ERR_SHAPE, "%s: hidden must be >= 1", name);
+    if (hidden > kMaxHidden)
+        return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
+    if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", name);   // 32-bit row loops
+    if (!z || !y || !mean || !rstd || !x || !bias || !residual || !gamma || !beta)
+        return fail(LS_ERR_NULL, "%s: null pointer", name);
+    const bool vec = hidden % 8 == 0 && aligned16(z) && aligned16(y) && aligned16(x) && aligned16(bias) &&
+                     aligned16(residual) && aligned16(gamma) && aligned16(beta);
+    LnShape s;
+    ln_shape(hidden, vec, &s);
+    const int threads = fwd_threads(rows, s, true);
+    const unsigned grid = fwd_grid(rows, s, threads);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto* y16 = static_cast<half_t*>(y);
+    auto* x16 = static_cast<const half_t*>(x);
+    auto* g16 = static_cast<const half_t*>(gamma);
+    auto* b16 = static_cast<const half_t*>(beta);
+    fz.z = static_cast<half_t*>(z);
+    fz.bias = static_cast<const half_t*>(bias);
+    fz.residual = static_cast<const half_t*>(residual);
+    const uint32_t r32 = static_cast<uint32_t>(rows), h32 = static_cast<uint32_t>(hidden);
+    clear_hip_error();
+    LS_LN_TABLE(LS_LN_FWD_FUSED)
+    char buf[112];
+    snprintf(buf, sizeof(buf), "bias_dropout_residual_layernorm/%s_b%d", s.name, threads);
     set_dispatch(buf);
     return launch_status(name);
 }

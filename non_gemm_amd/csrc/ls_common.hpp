@@ -193,6 +193,18 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// v of the first lane of this lane's aligned group of W lanes: a scalar read
+// of lane 0 for the whole wave, a ds_bpermute (no LDS access) for narrower
+// groups.  Every lane of the wave must be active.
+template <int W>
+__device__ __forceinline__ float group_first(float v, int lane) {
+    static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+    if constexpr (W == kWave)
+        return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+    else
+        return __shfl(v, lane & ~(W - 1));
+}
+
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
     static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");

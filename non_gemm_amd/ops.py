@@ -219,6 +219,26 @@ def layernorm_fwd(x, gamma, beta, eps, y=None, mean=None, rstd=None):
     return y, mean, rstd
 
 
+def bias_dropout_residual_layernorm(x, bias, residual, gamma, beta, p, seed, offset, eps, z=None, y=None,
+                                    mean=None, rstd=None):
+    """z = residual + Dropout(x + bias) and its LayerNorm, one launch.
+    Returns (z fp16, y fp16, mean fp32 [rows], rstd fp32 [rows])."""
+    _dev(x, bias, residual, gamma, beta, z, y, mean, rstd)
+    for t, n in ((x, "x"), (bias, "bias"), (residual, "residual"), (gamma, "gamma"), (beta, "beta")):
+        _dtype(t, _F16, n)
+    rows, h = _rows_cols(x)
+    if residual.shape != x.shape or bias.shape != (h,) or gamma.shape != (h,) or beta.shape != (h,):
+        raise ValueError("shape mismatch")
+    z = torch.empty_like(x) if z is None else z
+    y = torch.empty_like(x) if y is None else y
+    mean = torch.empty(rows, dtype=_F32, device=x.device) if mean is None else mean
+    rstd = torch.empty(rows, dtype=_F32, device=x.device) if rstd is None else rstd
+    check("ls_bias_dropout_residual_layernorm", load().ls_bias_dropout_residual_layernorm(
+        _ptr(z), _ptr(y), _ptr(mean), _ptr(rstd), _ptr(x), _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(beta),
+        rows, h, float(p), int(seed), int(offset), float(eps), _stream()))
+    return z, y, mean, rstd
+
+
 def layernorm_bwd_workspace_bytes(rows, hidden):
     return int(load().ls_layernorm_bwd_workspace_bytes(int(rows), int(hidden)))
 

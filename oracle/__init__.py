@@ -37,6 +37,7 @@ from .ops import (  # noqa: F401
     adam_workspace_step,
     bias_dropout_residual,
     bias_dropout_residual_bwd,
+    bias_dropout_residual_layernorm,
     bias_qkv_split,
     bias_qkv_split_bwd,
     bias_relu_dropout,

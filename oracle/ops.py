@@ -341,6 +341,23 @@ def layernorm_fwd(x, gamma, beta, eps):
     return y.astype(np.float16), mean.astype(np.float32), rstd.astype(np.float32)
 
 
+def bias_dropout_residual_layernorm(x, bias, residual, gamma, beta, p, seed, offset, bits, eps):
+    """z = residual + Dropout(x + bias), rounded to fp16, then LayerNorm of z.
+
+    The sub-layer output block of a post-LN Transformer layer ([LS2]
+    sec. 2.1.1: bias, dropout and residual add, then layer normalisation;
+    [L10] technique 1 fuses such neighbours).  The LayerNorm reads the stored
+    fp16 z, exactly as the two operators called one after the other.
+    Returns (z fp16, y fp16, mean fp32, rstd fp32).
+    Parity: the composition of bias_dropout_residual and layernorm_fwd, each
+    pinned on its own; pinned as a whole by tests against torch's float64
+    layer_norm of the fp16 sum (and constant residual rows giving beta).
+    """
+    z = bias_dropout_residual(x, bias, residual, p, seed, offset, bits)
+    y, mean, rstd = layernorm_fwd(z, gamma, beta, eps)
+    return z, y, mean, rstd
+
+
 def layernorm_bwd(dy, x, gamma, mean, rstd):
     """LayerNorm backward given the saved row statistics.
 

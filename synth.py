@@ -69,6 +69,21 @@ def uniform16(gen, shape, lo, hi):
     return gen.uniform(lo, hi, size=shape).astype(np.float16)
 
 
+# Ratios |mean| / std of the offset rows used to probe the one-pass variance.
+OFFSET_RATIOS = (0.0, 1.0, 3.0, 10.0, 30.0, 100.0, 1000.0)
+
+
+def offset_rows16(gen, rows, hidden, ratios=OFFSET_RATIOS, std=1.0):
+    """Rows ~ N(m_r, std) with m_r = +-ratio * std, the ratios taken in turn
+    and the sign alternating every len(ratios) rows (post-residual
+    activations whose mean is large next to their spread)."""
+    ratios = np.asarray(ratios, np.float64)
+    r = np.arange(rows)
+    sign = np.where((r // ratios.size) % 2 == 0, 1.0, -1.0)
+    means = sign * ratios[r % ratios.size] * std
+    return (means[:, None] + gen.normal(0.0, std, size=(rows, hidden))).astype(np.float16)
+
+
 def zipf_ids(gen, shape, vocab, s):
     """Token ids from a Zipf law truncated to ranks 1..vocab, P(k) ~ k^-s.
 

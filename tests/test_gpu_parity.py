@@ -415,6 +415,103 @@ def test_layernorm_bwd(ls, rows, h):
     assert np.array_equal(host(dx2), host(dx))
 
 
+LN_OFFSET_SHAPES = [(4096, 768), (448, 1024), (224, 256), (112, 96), (70, 4095), (56, 2048), (35, 13),
+                    (140, 767)]
+
+
+@pytest.mark.parametrize("rows,h", LN_OFFSET_SHAPES)
+def test_layernorm_offset_rows(ls, rows, h):
+    """Rows N(m, 1) with |m| / sigma in {0, 1, 3, 10, 30, 100, 1000}, both
+    signs: the one-pass statistics meet the fp32 bar (the reduction runs over
+    x minus the row's first element), and the outputs and the backward meet
+    the fp16 bar."""
+    g = np.random.default_rng(rows + 7 * h)
+    x = synth.offset_rows16(g, rows, h)
+    gamma = synth.uniform16(g, (h,), 0.5, 1.5)
+    beta = synth.normal16(g, (h,), 0.1)
+    dy = synth.normal16(g, (rows, h), 1.0)
+    y, mean, rstd = ls.layernorm_fwd(dev(x), dev(gamma), dev(beta), synth.LN_EPS)
+    ry, rmean, rrstd = oracle.layernorm_fwd(x, gamma, beta, synth.LN_EPS)
+    tag = f"layernorm_fwd offset rows {rows}x{h} [{last_dispatch()}]"
+    assert_fp16(host(y), ry, tag)
+    sigma = 1.0 / rrstd.astype(np.float64)
+    assert_fp32(host(mean), rmean, tag + " mean", floor=sigma)
+    assert_fp32(host(rstd), rrstd, tag + " rstd")
+    dx, dg, db = ls.layernorm_bwd(dev(dy), dev(x), dev(gamma), dev(rmean), dev(rrstd))
+    rdx, rdg, rdb = oracle.layernorm_bwd(dy, x, gamma, rmean, rrstd)
+    tag = f"layernorm_bwd offset rows {rows}x{h} [{last_dispatch()}]"
+    assert_fp16(host(dx), rdx, tag + " dx")
+    assert_fp16(host(dg), rdg, tag + " dgamma")
+    assert_fp16(host(db), rdb, tag + " dbeta")
+
+
+FUSED_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (77, 96), (33, 512), (9, 1536), (3, 4096), (20, 13),
+                (1030, 767), (5, 2048), (300, 768), (1, 8), (16384, 256), (4, 4095)]
+
+
+@pytest.mark.parametrize("rows,h", FUSED_SHAPES)
+@pytest.mark.parametrize("p", [0.1, 0.0, 1.0])
+def test_bias_dropout_residual_layernorm(ls, rows, h, p):
+    """The fused sub-layer output block against the oracle, and bit for bit
+    against the two separate operators called one after the other."""
+    g = np.random.default_rng(rows * 7 + h)
+    x, r = synth.normal16(g, (rows, h), 1.0), synth.normal16(g, (rows, h), 1.0)
+    b = synth.normal16(g, (h,), 0.02)
+    gamma, beta = synth.uniform16(g, (h,), 0.5, 1.5), synth.normal16(g, (h,), 0.1)
+    eps, off = synth.LN_EPS, synth.SITE_ATTN_OUT
+    z, y, mean, rstd = ls.bias_dropout_residual_layernorm(dev(x), dev(b), dev(r), dev(gamma), dev(beta), p, SEED,
+                                                          off, eps)
+    tag = f"bias_dropout_residual_layernorm {rows}x{h} p={p} [{last_dispatch()}]"
+    rz, ry, rmean, rrstd = oracle.bias_dropout_residual_layernorm(x, b, r, gamma, beta, p, SEED, off, BITS, eps)
+    assert_fp16(host(z), rz, tag + " z")
+    assert_fp16(host(y), ry, tag + " y")
+    sigma = 1.0 / rrstd.astype(np.float64)
+    assert_fp32(host(mean), rmean, tag + " mean", floor=sigma)
+    assert_fp32(host(rstd), rrstd, tag + " rstd")
+    z2 = ls.bias_dropout_residual(dev(x), dev(b), dev(r), p, SEED, off)
+    y2, mean2, rstd2 = ls.layernorm_fwd(z2, dev(gamma), dev(beta), eps)
+    assert np.array_equal(host(z).view(np.uint16), host(z2).view(np.uint16)), tag + ": z differs from the separate op"
+    assert np.array_equal(host(y).view(np.uint16), host(y2).view(np.uint16)), tag + ": y differs from the separate ops"
+    assert np.array_equal(host(mean), host(mean2)) and np.array_equal(host(rstd), host(rstd2)), tag
+
+
+def test_bias_dropout_residual_layernorm_aliasing_offsets_and_empty(ls):
+    """z written over the residual (in place) and over x; rows of the
+    residual offset by up to 1000 sigma; no rows launches nothing; bad
+    arguments are rejected before launching."""
+    from non_gemm_amd import _lib
+    rows, h, p, eps = 700, 768, 0.1, synth.LN_EPS
+    g = np.random.default_rng(41)
+    x = synth.normal16(g, (rows, h), 1.0)
+    r = synth.offset_rows16(g, rows, h)
+    b = synth.normal16(g, (h,), 0.02)
+    gamma, beta = synth.uniform16(g, (h,), 0.5, 1.5), synth.normal16(g, (h,), 0.1)
+    rz, ry, rmean, rrstd = oracle.bias_dropout_residual_layernorm(x, b, r, gamma, beta, p, SEED, 2, BITS, eps)
+    sigma = 1.0 / rrstd.astype(np.float64)
+    for target in ("residual", "x"):
+        xt, rt = dev(x), dev(r)
+        zt = rt if target == "residual" else xt
+        z, y, mean, rstd = ls.bias_dropout_residual_layernorm(xt, dev(b), rt, dev(gamma), dev(beta), p, SEED, 2,
+                                                              eps, z=zt)
+        tag = f"fused, z aliasing {target} [{last_dispatch()}]"
+        assert z.data_ptr() == zt.data_ptr()
+        assert_fp16(host(z), rz, tag + " z")
+        assert_fp16(host(y), ry, tag + " y")
+        assert_fp32(host(mean), rmean, tag + " mean", floor=sigma)
+        assert_fp32(host(rstd), rrstd, tag + " rstd")
+    e = torch.empty((0, h), dtype=torch.float16, device="cuda")
+    ls.bias_dropout_residual_layernorm(e, dev(b), e, dev(gamma), dev(beta), p, SEED, 2, eps)
+    assert last_dispatch() == "empty"
+    lib = _lib.load()
+    S = torch.cuda.current_stream().cuda_stream
+    t = dev(x)
+    for bad_p, bad_eps in ((1.5, eps), (0.1, 0.0)):
+        rc = lib.ls_bias_dropout_residual_layernorm(t.data_ptr(), t.data_ptr(), t.data_ptr(), t.data_ptr(),
+                                                    t.data_ptr(), t.data_ptr(), t.data_ptr(), t.data_ptr(),
+                                                    t.data_ptr(), rows, h, bad_p, SEED, 2, bad_eps, S)
+        assert rc == 3      # LS_ERR_PARAM
+
+
 def test_layernorm_bwd_workspace_reuse(ls):
     """One workspace serves calls of different shapes in turn (different
     block counts, so different partial-row layouts): each call is

@@ -253,6 +253,26 @@ def beam_candidates_unrounded(log_probs, beam_scores):
     return lp + np.asarray(beam_scores, np.float64)[:, :, None]
 
 
+def fused_ln_of_unrounded_sum(x, bias, residual, gamma, beta, p, seed, offset, bits, eps):
+    """Normalises the float64 sum instead of the stored fp16 z."""
+    x64, r64 = np.asarray(x, np.float64), np.asarray(residual, np.float64)
+    ms = _ms(x64.shape, p, seed, offset, bits)
+    z64 = r64 + ms * (x64 + np.asarray(bias, np.float64)[None, :])
+    mu = z64.mean(1, keepdims=True)
+    var = ((z64 - mu) ** 2).mean(1, keepdims=True)
+    rs = 1 / np.sqrt(var + float(np.float32(eps)))
+    y = (z64 - mu) * rs * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+    return z64.astype(np.float16), y.astype(np.float16), mu[:, 0].astype(np.float32), rs[:, 0].astype(np.float32)
+
+
+def fused_ln_without_residual(x, bias, residual, gamma, beta, p, seed, offset, bits, eps):
+    """Drops the residual from the normalised sum (z itself stays right)."""
+    z = oracle.bias_dropout_residual(x, bias, residual, p, seed, offset, bits)
+    branch = oracle.bias_dropout_residual(x, bias, np.zeros_like(residual), p, seed, offset, bits)
+    y, mean, rstd = oracle.layernorm_fwd(branch, gamma, beta, eps)
+    return z, y, mean, rstd
+
+
 def bdr_bwd_no_mask(dy, p, seed, offset, bits):
     """Passes dy through without the dropout mask."""
     dy64 = np.asarray(dy, np.float64)
@@ -354,6 +374,10 @@ def _cases():
                                                             (pins.test_xent_invariants_and_bad_targets, ())]),
         ("cross_entropy_bwd", xent_bwd_no_smoothing_floor, [(pins.test_xent_matches_torch_and_logsumexp, (0.1,)),
                                                              (pins.test_xent_invariants_and_bad_targets, ())]),
+        ("bias_dropout_residual_layernorm", fused_ln_of_unrounded_sum,
+         [(pins.test_bias_dropout_residual_layernorm_against_torch, (0.1,))]),
+        ("bias_dropout_residual_layernorm", fused_ln_without_residual,
+         [(pins.test_bias_dropout_residual_layernorm_against_torch, (0.0,))]),
         ("beam_candidates", beam_candidates_sign_flipped, [(golden.test_beam_candidates_hand_computed, ()),
                                                            (pins.test_hars_equals_full_sort, (3, 4, 50, 4))]),
         ("beam_candidates", beam_candidates_unrounded, [(golden.test_beam_candidates_hand_computed, ())]),

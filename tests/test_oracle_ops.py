@@ -360,6 +360,35 @@ def test_ln_matches_torch_and_one_pass():
     np.testing.assert_allclose(mu1, mean, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("p", [0.0, 0.1])
+def test_bias_dropout_residual_layernorm_against_torch(p):
+    """The fused sub-layer output block: torch float64 for the sum (rounded to
+    fp16, the stored z) and for layer_norm; the mask from the Philox keep
+    function (pinned against rocRAND's engine) and the page-derived scale."""
+    g = np.random.default_rng(12)
+    rows, h, seed, off = 40, 96, 0x1234, 2
+    x, r = f16(g.normal(size=(rows, h))), f16(g.normal(size=(rows, h)))
+    b, gamma, beta = f16(g.normal(0, 0.02, h)), f16(g.uniform(0.5, 1.5, h)), f16(g.normal(0, 0.1, h))
+    eps = 1e-5
+    z, y, mean, rstd = oracle.bias_dropout_residual_layernorm(x, b, r, gamma, beta, p, seed, off, 16, eps)
+    keep = dropout_keep(np.arange(rows * h, dtype=np.uint64), p, seed, off, 16).reshape(rows, h)
+    t = lambda a: torch.tensor(np.asarray(a, np.float64))  # noqa: E731
+    zt = t(r) + t(keep) * dropout_scale(p, 16) * (t(x) + t(b))
+    z_ref = zt.numpy().astype(np.float16)
+    np.testing.assert_array_equal(z, z_ref)
+    z64 = t(z_ref)
+    y_ref = torch.nn.functional.layer_norm(z64, (h,), t(gamma), t(beta), float(np.float32(eps)))
+    np.testing.assert_array_equal(y, y_ref.numpy().astype(np.float16))
+    var, mu = torch.var_mean(z64, dim=1, unbiased=False)
+    np.testing.assert_allclose(mean, mu.numpy(), rtol=1e-7, atol=1e-9)
+    np.testing.assert_allclose(rstd, (1 / torch.sqrt(var + float(np.float32(eps)))).numpy(), rtol=1e-7)
+    # a constant residual row with x + bias = 0 everywhere normalises to beta
+    z, y, _, _ = oracle.bias_dropout_residual_layernorm(np.zeros((2, h), np.float16), np.zeros(h, np.float16),
+                                                        np.full((2, h), 3.0, np.float16), gamma, beta, p, seed, off,
+                                                        16, eps)
+    assert np.all(z == np.float16(3.0)) and np.array_equal(y, np.broadcast_to(beta, y.shape))
+
+
 def _ln_fwd64(x, gamma, beta, eps):
     mu = x.mean(-1, keepdims=True)
     var = ((x - mu) ** 2).mean(-1, keepdims=True)
