@@ -70,6 +70,9 @@ def chain_bytes(tokens, hidden, ffn, heads, seq, fused=True):
         "bias_dropout_residual_layernorm": 8 * e_h + 8 * rows + 6 * hidden,
         "bias_relu_dropout": 4 * e_f + 2 * ffn,                   # x, out (+bias)
         "layernorm_bwd": 6 * e_h + 8 * rows + 6 * hidden,         # dy, x, dx, stats, gamma, dgamma, dbeta
+        # its two calls: the input gradient (row kernel) and the parameter gradients
+        "layernorm_bwd_input": 6 * e_h + 8 * rows + 2 * hidden,
+        "layernorm_bwd_params": 4 * hidden,
         "softmax_bwd": 6 * e_s,                                   # y, dy, dx
     }
     counts = {"softmax_fwd": 1, "bias_relu_dropout": 1, "layernorm_bwd": 2, "softmax_bwd": 1}
@@ -150,6 +153,7 @@ class ChainSet:
 
     def __init__(self, torch, inputs, shape, lib, per_bytes, p, seed, eps, fused=True):
         d = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+        self.torch = torch
         self.t = {k: d(v) for k, v in inputs.items()}
         t = self.t
         T, H, F = shape.tokens, shape.hidden, shape.ffn
@@ -204,20 +208,73 @@ class ChainSet:
             ("bias_relu_dropout", pb["bias_relu_dropout"], lib.ls_bias_relu_dropout,
              (P["ffn_act"], P["ffn_pre"], P["ffn_bias1"], T, F, p, seed, synth.SITE_FFN_ACT, S)),
             *sub2,
-            ("layernorm_bwd", pb["layernorm_bwd"], lib.ls_layernorm_bwd,
-             (P["dx2"], P["dg2"], P["db2"], P["grad_y2"], P["ffn_out"], P["gamma2"], P["mean2"], P["rstd2"],
-              T, H, P["ws2"], ws, S)),
-            ("layernorm_bwd", pb["layernorm_bwd"], lib.ls_layernorm_bwd,
-             (P["dx1"], P["dg1"], P["db1"], P["grad_y1"], P["attn_out"], P["gamma1"], P["mean1"], P["rstd1"],
-              T, H, P["ws1"], ws, S)),
+            # LayerNorm backward as its two calls: the input gradient, then the
+            # parameter gradients (consumed only by the optimizer; tagged so a
+            # caller may put them on a side stream).
+            ("layernorm_bwd", pb["layernorm_bwd_input"], lib.ls_layernorm_bwd_input,
+             (P["dx2"], P["grad_y2"], P["ffn_out"], P["gamma2"], P["mean2"], P["rstd2"], T, H, P["ws2"], ws, S)),
+            ("layernorm_bwd_params", pb["layernorm_bwd_params"], lib.ls_layernorm_bwd_params,
+             (P["dg2"], P["db2"], T, H, P["ws2"], ws, S), "side"),
+            ("layernorm_bwd", pb["layernorm_bwd_input"], lib.ls_layernorm_bwd_input,
+             (P["dx1"], P["grad_y1"], P["attn_out"], P["gamma1"], P["mean1"], P["rstd1"], T, H, P["ws1"], ws, S)),
+            ("layernorm_bwd_params", pb["layernorm_bwd_params"], lib.ls_layernorm_bwd_params,
+             (P["dg1"], P["db1"], T, H, P["ws1"], ws, S), "side"),
             ("softmax_bwd", pb["softmax_bwd"], lib.ls_softmax_bwd,
              (P["dscores"], P["probs"], P["grad_probs"], B * NH * L, L, S)),
         ]
 
-    def run(self, check, names=None):
-        for name, _, fn, args in self.launches:
-            if names is None or name in names:
-                check(name, fn(*args))
+    def run(self, check, side=None):
+        issue(self.torch, self.launches, check, side)
+
+
+def op_of(item_name):
+    """The operator a launch item belongs to (the LayerNorm backward's
+    parameter call is part of layernorm_bwd)."""
+    return item_name[:-len("_params")] if item_name.endswith("_params") else item_name
+
+
+def issue(torch, items, check, side=None):
+    """Issues launch items (name, bytes, fn, args[, "side"]) on the current
+    stream, the stream argument (the last of args) replaced by the stream
+    used.  Items tagged "side" go to the side stream after an event on the
+    current one, and the current stream waits for the side stream at the end;
+    with side=None they run in order on the current stream."""
+    main = torch.cuda.current_stream()
+    forked = False
+    for it in items:
+        name, _, fn, a = it[:4]
+        if len(it) > 4 and side is not None:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                check(name, fn(*a[:-1], side.cuda_stream))
+            forked = True
+        else:
+            check(name, fn(*a[:-1], main.cuda_stream))
+    if forked:
+        main.wait_stream(side)
+
+
+def capture_items(torch, items, cap_stream, check, side):
+    """One HIP graph of the launch items (side-stream items as a branch that
+    joins before the graph ends)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap_stream):
+        issue(torch, items, check, side)
+    return g
+
+
+def replay_us(torch, graphs, reps):
+    """Mean microseconds per graph over reps rounds of the graphs in turn."""
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(graphs))
 
 
 def build_sets(torch, lib, shape, nsets, p, seed, eps, config=3, fused=True):
@@ -694,7 +751,7 @@ def stored_traffic():
 
 # ---------------------------------------------------------------------------
 
-def transformer_big_chain(torch, lib, check, cap_stream, p, seed, eps, nsets=3, reps=20):
+def transformer_big_chain(torch, lib, check, cap_stream, side, p, seed, eps, nsets=3, reps=20):
     """The Transformer-big layer (8192 tokens, hidden 1024, 16 heads, FFN 4096)
     through the same 11 launches plus the embedding forward and backward
     (vocabulary 32768, Zipf ids, fp32 gradient accumulated), one HIP graph per
@@ -724,30 +781,14 @@ def transformer_big_chain(torch, lib, check, cap_stream, p, seed, eps, nsets=3, 
         s.launches.append(("embedding_bwd", emb_b, lib.ls_embedding_bwd,
                            (dE.data_ptr(), ids.data_ptr(), dy.data_ptr(), shape.batch, L, H, V, inp["scale"], p, seed,
                             synth.SITE_EMBEDDING, 0, S)))
-        s.run(check)
+        s.run(check, side)
     torch.cuda.synchronize()
-    graphs = []
-    for s in sets:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
-            st = torch.cuda.current_stream().cuda_stream
-            for nm, _, fn, a in s.launches:
-                check(nm, fn(*a[:-1], st))
-        graphs.append(g)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps * len(graphs)):
-        graphs[i % len(graphs)].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * len(graphs))
+    graphs = [capture_items(torch, s.launches, cap_stream, check, side) for s in sets]
+    us = replay_us(torch, graphs, reps)
     nbytes = total + emb_f + emb_b
     out = {"shape": "8192 tokens (32 x 256), hidden 1024, 16 heads, FFN 4096, vocab 32768",
            "calls_per_step": len(sets[0].launches),
-           "kernels_per_step": len(sets[0].launches) + counts["layernorm_bwd"],   # + LayerNorm's column sums
+           "kernels_per_step": len(sets[0].launches),
            "us_per_step": round(us, 2), "bytes_per_step": nbytes,
            "GB/s": round(nbytes / us / 1e3, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
            "rotated_sets": nsets}
@@ -796,47 +837,32 @@ def attainable(torch, lib, check, cap_stream, dom_bytes):
     return out
 
 
-def unfused_chain(torch, lib, check, cap_stream, p, seed, eps, nsets=12, reps=20):
-    """The same BERT-base step with bias+dropout+residual and LayerNorm as two
-    operators each (11 calls per step), on its own rotated sets: the
-    comparison point for the fused step."""
+def step_variants(torch, lib, check, cap_stream, p, seed, eps, nsets=12, reps=20):
+    """The same BERT-base step in two other forms, each on its own rotated
+    sets: bias+dropout+residual and LayerNorm as two operators each
+    (unfused), and the fused step with the LayerNorm parameter gradients on a
+    side stream (a branch of the graph, joined at the end of the step)."""
     import synth
     shape = synth.C3
-    sets, per, counts, total = build_sets(torch, lib, shape, nsets, p, seed, eps, fused=False)
-    for s in sets:
-        s.run(check)
-    graphs = []
-    for s in sets:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
-            st = torch.cuda.current_stream().cuda_stream
-            for nm, _, fn, a in s.launches:
-                check(nm, fn(*a[:-1], st))
-        graphs.append(g)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps * len(graphs)):
-        graphs[i % len(graphs)].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * len(graphs))
-    out = {"calls_per_step": len(sets[0].launches), "us_per_step": round(us, 2), "bytes_per_step": total,
-           "GB/s": round(total / us / 1e3, 1), "tokens_per_s": round(shape.tokens / (us * 1e-6), 1)}
-    del graphs, sets
-    torch.cuda.empty_cache()
+    out = {}
+    side = torch.cuda.Stream()         # default priority, like every stream here
+    for fused, side_ in ((False, None), (True, side)):
+        sets, per, counts, total = build_sets(torch, lib, shape, nsets, p, seed, eps, fused=fused)
+        for s in sets:
+            s.run(check, side_)
+        graphs = [capture_items(torch, s.launches, cap_stream, check, side_) for s in sets]
+        us = replay_us(torch, graphs, reps)
+        key = "unfused" if not fused else "fused_parameter_gradients_on_side_stream"
+        out[key] = {"calls_per_step": len(sets[0].launches), "us_per_step": round(us, 2), "bytes_per_step": total,
+                    "GB/s": round(total / us / 1e3, 1), "tokens_per_s": round(shape.tokens / (us * 1e-6), 1)}
+        del graphs, sets
+        torch.cuda.empty_cache()
     return out
 
 
-def warm_chain_us(torch, s, cap_stream, check, reps=100):
+def warm_chain_us(torch, s, cap_stream, check, side, reps=100):
     """One buffer set replayed back to back: the chain with its tensors cache-resident."""
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=cap_stream):
-        st = torch.cuda.current_stream().cuda_stream
-        for nm, _, fn, a in s.launches:
-            check(nm, fn(*a[:-1], st))
+    g = capture_items(torch, s.launches, cap_stream, check, side)
     g.replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -897,8 +923,12 @@ def main():
 
     sets, per, counts, total = build_sets(torch, lib, shape, args.sets, p, seed, eps)
     footprint = sum(sum(t.numel() * t.element_size() for t in s.t.values()) for s in sets)
+    # The step runs on one stream: the LayerNorm parameter gradients in line.
+    # (A side-stream branch for them, joined at the end of the step, measured
+    # 94 against 62 us per step: see step_variants.)
+    side = None
     for s in sets:                     # first launches outside any capture
-        s.run(check)
+        s.run(check, side)
     torch.cuda.synchronize()
 
     # Per set: one graph of the whole step, and the same step split around the
@@ -910,12 +940,7 @@ def main():
     cap_stream = torch.cuda.Stream()
 
     def capture(s, lo, hi):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
-            st = torch.cuda.current_stream().cuda_stream
-            for name, _, fn, a in s.launches[lo:hi]:
-                check(name, fn(*a[:-1], st))
-        return g
+        return capture_items(torch, s.launches[lo:hi], cap_stream, check, side)
     n_launch = len(sets[0].launches)
     graphs = [(capture(s, 0, n_launch), capture(s, 0, dom_idx), capture(s, dom_idx + 1, n_launch)) for s in sets]
     torch.cuda.synchronize()
@@ -933,16 +958,14 @@ def main():
             return
         fn, a = dom[i % len(dom)]
         if args.eager:
-            for nm, _, f, aa in s.launches[:dom_idx]:
-                f(*aa)
+            issue(torch, s.launches[:dom_idx], check, side)
         else:
             g_a.replay()
         if sampled:
             ev.arm(i // SAMPLE, lib)
         fn(*a)
         if args.eager:
-            for nm, _, f, aa in s.launches[dom_idx + 1:]:
-                f(*aa)
+            issue(torch, s.launches[dom_idx + 1:], check, side)
         else:
             g_b.replay()
 
@@ -965,20 +988,16 @@ def main():
     ms_step = gpu_ms / K
     dom_us = kev.mean_us()
     kev.close()
-    dom_bytes = per[DOMINANT]
+    dom_bytes = per[DOMINANT + "_input"]        # the row kernel's own bytes (dgamma/dbeta come from the params call)
     achieved = dom_bytes / dom_us / 1e3          # GB/s
 
     # Informational: per-kernel cold times (graphs of R launches of one kind) and
     # the warm (single buffer set) chain.
     kernels = {}
     for name in ([] if args.no_info else counts):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
-            st = torch.cuda.current_stream().cuda_stream
-            for s in sets:
-                for nm, _, fn, a in s.launches:
-                    if nm == name:
-                        check(nm, fn(*a[:-1], st))
+        # the whole operator, its calls in order on one stream
+        g = capture_items(torch, [it for s in sets for it in s.launches if op_of(it[0]) == name], cap_stream, check,
+                          None)
         g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1001,17 +1020,19 @@ def main():
                    "timing": "cold: a graph of back-to-back launches over the rotated sets, events around it"}
     warm_us = None
     if not args.no_info:
-        warm_us = warm_chain_us(torch, sets[0], cap_stream, check)
+        warm_us = warm_chain_us(torch, sets[0], cap_stream, check, side)
     dispatch = {}
-    for name, _, fn, args_ in sets[0].launches:
-        fn(*args_)
+    for it in sets[0].launches:
+        name, _, fn, args_ = it[:4]
+        check(name, fn(*args_))
         dispatch[name] = _lib.last_dispatch()
     torch.cuda.synchronize()
     del graphs, sets
     torch.cuda.empty_cache()
-    unfused = None if args.no_info else unfused_chain(torch, lib, check, cap_stream, p, seed, eps, nsets=args.sets)
-    reach = None if args.no_info else attainable(torch, lib, check, cap_stream, per[DOMINANT])
-    big = None if args.no_info else transformer_big_chain(torch, lib, check, cap_stream, p, seed, eps)
+    variants = None if args.no_info else step_variants(torch, lib, check, cap_stream, p, seed, eps,
+                                                       nsets=args.sets)
+    reach = None if args.no_info else attainable(torch, lib, check, cap_stream, dom_bytes)
+    big = None if args.no_info else transformer_big_chain(torch, lib, check, cap_stream, side, p, seed, eps)
 
     extra = None if args.no_extra else extra_rows(torch, ops)
     cpu = None if args.no_cpu else cpu_baseline(shape, p, seed, eps)
@@ -1043,14 +1064,20 @@ def main():
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": stored_traffic(), "algorithmic_bytes": dom_bytes,
-                     "avg_duration_us": round(dom_us, 3)},
+                     "avg_duration_us": round(dom_us, 3),
+                     # the whole operator (row kernel, then its parameter finalisation on the same stream),
+                     # from the cold per-operator timing
+                     "op_level": None if DOMINANT not in kernels else {
+                         "algorithmic_bytes": per[DOMINANT], "us": kernels[DOMINANT]["us"],
+                         "achieved": kernels[DOMINANT]["GB/s"],
+                         "frac": round(kernels[DOMINANT]["GB/s"] / HBM_PEAK_GBPS, 4)}},
         "roofline_largest_launch": largest,
         "cpu_baseline": cpu,
         "kernels_cold": kernels,
         "warm_chain_us": None if warm_us is None else round(warm_us, 2),
         "attainable_hbm": reach,
         "dispatch": dispatch,
-        "unfused_chain": unfused,
+        "step_variants": variants,
         "transformer_big_chain": big,
         "other_rows": extra,
         "wall_s_timed": round(wall, 4),

@@ -227,6 +227,8 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
  * element index row * hidden + col, site `offset`).  z may alias x or
  * residual; y must not alias any input.
  * p in [0, 1], eps > 0, hidden in [1, 4096], rows < 2^31.
+ * One launch; element-wise rows (hidden % 8 != 0 or a pointer not 16-byte
+ * aligned) longer than 2048 take the two standalone operators' launches.
  * Errors: LS_ERR_SHAPE, LS_ERR_PARAM, LS_ERR_UNSUPPORTED (hidden > 4096),
  * LS_ERR_NULL.  rows == 0 launches nothing. */
 int ls_bias_dropout_residual_layernorm(void* z, void* y, float* mean, float* rstd, const void* x,
@@ -234,9 +236,10 @@ int ls_bias_dropout_residual_layernorm(void* z, void* y, float* mean, float* rst
                                        const void* beta, int64_t rows, int64_t hidden, float p, uint64_t seed,
                                        uint64_t offset, float eps, void* stream);
 
-/* Bytes of device scratch that ls_layernorm_bwd needs for this shape
- * (per-block fp32 column partials of dgamma and dbeta).  Depends only on
- * (rows, hidden).  Returns 0 for invalid or empty shapes. */
+/* Bytes of device scratch that ls_layernorm_bwd needs for this shape: a
+ * 256-byte header (the partial-row count) and the per-block fp32 column
+ * partials of dgamma and dbeta.  Depends only on (rows, hidden).  Returns 0
+ * for invalid or empty shapes. */
 size_t ls_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
 
 /* LayerNorm backward ([L10] technique 2, slide 22).  With
@@ -249,11 +252,36 @@ size_t ls_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
  * [hidden]; mean, rstd: fp32 [rows] from ls_layernorm_fwd.  dx may alias dy.
  * workspace: device scratch of at least ls_layernorm_bwd_workspace_bytes()
  * bytes, 16-byte aligned; its contents on entry are ignored.
- * rows < 2^31 (else LS_ERR_SHAPE).
- * Two kernel launches (row pass, then column finalisation). */
+ * rows < 2^31 (else LS_ERR_SHAPE).  rows == 0 writes zeros to dgamma and
+ * dbeta (the sum over no rows; workspace may then be NULL) and touches
+ * nothing else.
+ * Exactly ls_layernorm_bwd_input followed by ls_layernorm_bwd_params on the
+ * same stream: two kernel launches (row pass, then column finalisation). */
 int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
                      const void* gamma, const float* mean, const float* rstd, int64_t rows,
                      int64_t hidden, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of ls_layernorm_bwd, for callers that keep the parameter
+ * gradients off the critical path: only the input gradient dx feeds the
+ * rest of the backward pass, while dgamma / dbeta wait for the optimizer, so
+ * the finalisation may run on another stream (ordered after the input call
+ * by an event) while the next operators proceed.
+ * ls_layernorm_bwd_input: dx, and the fixed-order per-block column partials
+ * plus their count into workspace (arguments and errors as ls_layernorm_bwd;
+ * rows == 0 launches nothing).
+ * ls_layernorm_bwd_params: dgamma, dbeta from the partials of the input call
+ * with the same (rows, hidden) and workspace, which must be complete (same
+ * stream, or an event) and not overwritten before this call runs.  rows == 0
+ * writes zeros without reading the workspace (it may be NULL).  A workspace
+ * not written by a matching input call gives unspecified values, but every
+ * read stays inside workspace_bytes.
+ * Errors: LS_ERR_SHAPE, LS_ERR_UNSUPPORTED (hidden > 4096), LS_ERR_NULL,
+ * LS_ERR_WORKSPACE, LS_ERR_PARAM (misaligned workspace). */
+int ls_layernorm_bwd_input(void* dx, const void* dy, const void* x, const void* gamma, const float* mean,
+                           const float* rstd, int64_t rows, int64_t hidden, void* workspace, size_t workspace_bytes,
+                           void* stream);
+int ls_layernorm_bwd_params(void* dgamma, void* dbeta, int64_t rows, int64_t hidden, const void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Masked row softmax forward ([L10] slides 23-26) over attention scores
  * x, y: fp16 [batch, heads, q_len, k_len].  For row (b, h, i) the valid keys

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kBlock) void adam_scalar_kernel(half_t* p, const ha
     for (uint64_t i = first + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
         float mi = m[i], vi = v[i];
         const float pn = adam_one<DECOUPLED>(static_cast<float>(p[i]), static_cast<float>(g[i]), mi, vi, a);
-        p[i] = static_cast<half_t>(pn);
+        p[i] = to_half(pn);
         m[i] = mi;
         v[i] = vi;
     }
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(half_t* p, const half_t* g
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float mk = mq[q][k], vk = vq[q][k];
-                pq[q][k] = static_cast<half_t>(adam_one<DECOUPLED>(static_cast<float>(pq[q][k]),
+                pq[q][k] = to_half(adam_one<DECOUPLED>(static_cast<float>(pq[q][k]),
                                                                    static_cast<float>(gq[q][k]), mk, vk, a));
                 mq[q][k] = mk;
                 vq[q][k] = vk;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(half_t* p, const half_t* g
         for (uint64_t i = n4 + threadIdx.x; i < n; i += kBlock) {
             float mi = m[i], vi = v[i];
             const float pn = adam_one<DECOUPLED>(static_cast<float>(p[i]), static_cast<float>(g[i]), mi, vi, a);
-            p[i] = static_cast<half_t>(pn);
+            p[i] = to_half(pn);
             m[i] = mi;
             v[i] = vi;
         }

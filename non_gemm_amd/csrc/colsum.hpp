@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kFinCols * kFinSlices) void colsum_finalize_kernel(
         float t = 0.0f;
 #pragma unroll
         for (int s = 0; s < kFinSlices; ++s) t += sums[s][cl];
-        out[c] = static_cast<half_t>(t);
+        out[c] = to_half(t);
     }
 }
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kBlock) void elementwise_scalar_kernel(
         if (RELU) t = t < 0.0f ? 0.0f : t;
         const float f = DROP ? dropout_factor1(d, i) : 1.0f;
         const float o = RESID ? fmaf(f, t, static_cast<float>(res[i])) : t * f;
-        out[i] = static_cast<half_t>(o);
+        out[i] = to_half(o);
     }
 }
 

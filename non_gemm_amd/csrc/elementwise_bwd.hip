@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void ew_bwd_scalar_kernel(half_t* dx, float* p
         const float f = RELU ? (static_cast<float>(out[i]) > 0.0f ? d.scale : 0.0f) : dropout_factor1(d, i);
         const float o = static_cast<float>(dy[i]) * f;
         acc += o;
-        dx[i] = static_cast<half_t>(o);
+        dx[i] = to_half(o);
     }
     partial[static_cast<size_t>(blockIdx.y) * cols + c] = acc;
 }

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void emb_fwd_scalar_kernel(half_t* out, con
         } else {
             o = __builtin_nanf("");
         }
-        out[i] = static_cast<half_t>(o);
+        out[i] = to_half(o);
     }
 }
 

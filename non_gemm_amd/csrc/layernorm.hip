@@ -62,7 +62,7 @@ struct Chunk<1> {
         f[0] = static_cast<float>(p[i]);
     }
     static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[1]) {
-        p[i] = static_cast<half_t>(f[0]);
+        p[i] = to_half(f[0]);
     }
 };
 
@@ -148,6 +148,9 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
             // the tensor, out-of-range values zeroed afterwards (a load
             // under a branch gets its conversion moved into the branch, a
             // wait per element).
+            // (The fused form loads gamma and beta only after z is formed,
+            // below, so that x, residual, bias, gamma and beta are never all
+            // held at once.)
             const size_t cbase = static_cast<size_t>(ok ? row : rows - 1) * h;
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
@@ -157,9 +160,10 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
                 if constexpr (FUSED) {
                     rr[j] = R::load_cached(fz.residual, cbase + cc);
                     cr[j] = R::load_cached(fz.bias, cc);
+                } else {
+                    gr[j] = R::load_cached(gamma, cc);
+                    br[j] = R::load_cached(beta, cc);
                 }
-                gr[j] = R::load_cached(gamma, cc);
-                br[j] = R::load_cached(beta, cc);
             }
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
@@ -168,9 +172,10 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
                 if constexpr (FUSED) {
                     rr[j] = in ? rr[j] : R::zero();
                     cr[j] = in ? cr[j] : R::zero();
+                } else {
+                    gr[j] = in ? gr[j] : R::zero();
+                    br[j] = in ? br[j] : R::zero();
                 }
-                gr[j] = in ? gr[j] : R::zero();
-                br[j] = in ? br[j] : R::zero();
             }
         } else {
 #pragma unroll
@@ -200,11 +205,32 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
                 }
             }
         }
+        // The dropout words of every chunk, computed while the loads are in
+        // flight (they depend on the element index only).  With p = 0 the
+        // threshold is 0 and every field keeps its element at scale 1, so no
+        // branch is needed.
+        // (The element-wise path computes each element's factor where it is
+        // used: holding a field per element would cost a register each.)
+        uint32_t dw[CW == 8 ? NF : 1][4];
+        if constexpr (FUSED && CW == 8) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const uint64_t i0 = static_cast<uint64_t>(row) * h + (l + j * LPR) * CW;   // flat index
+                dropout_words(fz.d, i0 >> 3, dw[j]);                       // h % 8 == 0: one Philox call
+            }
+            // Keep the rounds here, ahead of the first wait for the loads: the
+            // words pass through an empty asm statement (no instruction), so
+            // the compiler cannot sink later chunks' rounds into the blocks
+            // that use them, after the wait.
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(dw[j][q]));
+        }
         float v[NCH][CW];
         if constexpr (FUSED) {
             // z = residual + keep * (x + bias) * scale, rounded to fp16 and
             // stored; the statistics and y use the stored value.
-            const bool drop = fz.d.thr != 0;
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
                 const uint32_t c = (l + j * LPR) * CW;
@@ -212,15 +238,8 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
                 R::widen(xr[j], a);
                 R::widen(cr[j], b);
                 R::widen(rr[j], r);
-                const uint64_t i0 = static_cast<uint64_t>(row) * h + c;    // flat index of the chunk
-                if constexpr (CW == 8) {
-                    if (drop) dropout_factors8(fz.d, i0 >> 3, f);          // h % 8 == 0: one Philox call
-                    else
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) f[k] = 1.0f;
-                } else {
-                    f[0] = drop ? dropout_factor1(fz.d, i0) : 1.0f;
-                }
+                if constexpr (CW == 8) dropout_factors_from(fz.d, dw[j], f);
+                else f[0] = dropout_factor1(fz.d, static_cast<uint64_t>(row) * h + c);
 #pragma unroll
                 for (int k = 0; k < CW; ++k) o[k] = fmaf(f[k], a[k] + b[k], r[k]);
                 if constexpr (CW == 8) {
@@ -228,9 +247,26 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
                     if (ok && c < h) __builtin_nontemporal_store(zh, reinterpret_cast<half8*>(fz.z + base + c));
                     unpack8(zh, v[j]);
                 } else {
-                    const half_t zh = static_cast<half_t>(o[0]);
+                    const half_t zh = to_half(o[0]);
                     if (ok && c < h) fz.z[base + c] = zh;
                     v[j][0] = static_cast<float>(zh);
+                }
+            }
+            if constexpr (CW == 1) {
+                // gamma and beta for the element-wise path (cache hits), at
+                // clamped indices, zero outside the row
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) {
+                    const uint32_t c = l + j * LPR;
+                    const uint32_t cc = c < h ? c : h - 1;
+                    gr[j] = R::load_cached(gamma, cc);
+                    br[j] = R::load_cached(beta, cc);
+                }
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) {
+                    const bool in = ok && l + j * LPR < h;
+                    gr[j] = in ? gr[j] : R::zero();
+                    br[j] = in ? br[j] : R::zero();
                 }
             }
         } else {
@@ -243,13 +279,15 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
         // the size of the row's spread rather than of its mean (shifted data,
         // Chan, Golub & LeVeque 1983), so rows whose |mean| is large next to
         // their spread keep fp32 accuracy.
+        // Lane slots past the end of the row hold zeros and must stay zero
+        // after the shift.
         const float K = group_first<LPR>(v[0][0], lane);
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NCH; ++j)
 #pragma unroll
             for (int k = 0; k < CW; ++k) {
-                v[j][k] -= K;
+                v[j][k] = (l + j * LPR) * CW < h ? v[j][k] - K : 0.0f;
                 s1 += v[j][k];
                 s2 = fmaf(v[j][k], v[j][k], s2);
             }
@@ -307,10 +345,13 @@ constexpr size_t kBwdLdsBudget = 128 * 1024;
 
 template <int LPR, int NCH, int CW>
 __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kernel(half_t* dx, float* partial,
-                                                                const half_t* dy, const half_t* x,
-                                                                const half_t* gamma, const float* mean,
-                                                                const float* rstd, uint32_t rows,
-                                                                uint32_t h) {
+                                                                uint32_t* header, const half_t* dy,
+                                                                const half_t* x, const half_t* gamma,
+                                                                const float* mean, const float* rstd,
+                                                                uint32_t rows, uint32_t h) {
+    // The partial-row count, for the finalisation (which may run as a
+    // separate call).
+    if (blockIdx.x == 0 && threadIdx.x == 0) header[0] = gridDim.x;
     // Element-wise rows of up to 2048: one register per element and clamped
     // unconditional loads; longer ones are read twice (kTwoPass).
     constexpr bool kClamped = CW == 1 && NCH <= 32;
@@ -570,9 +611,15 @@ constexpr int kFinCols = 32;
 constexpr int kFinSlices = 16;
 constexpr unsigned kMaxBwdBlocks = kFinSlices * 16;
 
+// The partial-row count comes from the workspace header the row kernel
+// wrote, clamped to max_blocks (the count the workspace is sized for), so a
+// stale header cannot send a read past the partial rows; max_blocks == 0
+// (no rows) writes zeros without reading the workspace.
 __global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
-    half_t* dgamma, half_t* dbeta, const float* partial, uint32_t nblocks, uint32_t h) {
+    half_t* dgamma, half_t* dbeta, const uint32_t* header, const float* partial, uint32_t max_blocks,
+    uint32_t h) {
     __shared__ float sums[kFinSlices][kFinCols];
+    const uint32_t nblocks = max_blocks ? min(header[0], max_blocks) : 0u;
     const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
     const uint32_t c = blockIdx.x * kFinCols + cl;
     const uint32_t w = 2 * h;
@@ -591,8 +638,8 @@ __global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
         float t = 0.0f;
 #pragma unroll
         for (int s = 0; s < kFinSlices; ++s) t += sums[s][cl];
-        if (c < h) dgamma[c] = static_cast<half_t>(t);
-        else dbeta[c - h] = static_cast<half_t>(t);
+        if (c < h) dgamma[c] = to_half(t);
+        else dbeta[c - h] = to_half(t);
     }
 }
 
@@ -629,6 +676,10 @@ bool ln_shape(int64_t h, bool vec, LnShape* s) {
 }
 
 constexpr int64_t kMaxHidden = 4096;
+constexpr size_t kBwdHeaderBytes = 256;       // partial rows start 256 bytes in
+inline unsigned bwd_max_blocks(int64_t rows) {
+    return static_cast<unsigned>(rows < kMaxBwdBlocks ? rows : kMaxBwdBlocks);
+}
 constexpr int kNumCU = 256;
 
 unsigned fwd_grid(int64_t rows, const LnShape& s, int threads) {
@@ -638,10 +689,11 @@ unsigned fwd_grid(int64_t rows, const LnShape& s, int threads) {
 }
 
 // 1024-thread blocks when the shape allows them and the rows fill every CU
-// with one; 256 otherwise.
+// with one; 256 otherwise.  The fused form always takes 256 (measured
+// 7.1 against 7.3 us at 4096 x 768, 14.6 against 15.0 at 8192 x 1024).
 int fwd_threads(int64_t rows, const LnShape& s, bool fused) {
     const int64_t rows_per_big = kFwdBig / kWave * (kWave / s.lpr);
-    return fwd_big_ok(s.nch, s.cw, fused) && rows >= kNumCU * rows_per_big ? kFwdBig : kFwdSmall;
+    return !fused && fwd_big_ok(s.nch, s.cw, fused) && rows >= kNumCU * rows_per_big ? kFwdBig : kFwdSmall;
 }
 
 template <int LPR, int NCH, int CW, bool FUSED>
@@ -687,8 +739,11 @@ BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
 
 #define LS_LN_FWD(LPR, NCH, CW) \
     launch_ln_fwd<LPR, NCH, CW, false>(threads, grid, st, y16, mean, rstd, x16, g16, b16, r32, h32, eps, fz)
-#define LS_LN_FWD_FUSED(LPR, NCH, CW) \
-    launch_ln_fwd<LPR, NCH, CW, true>(threads, grid, st, y16, mean, rstd, x16, g16, b16, r32, h32, eps, fz)
+#define LS_LN_FWD_FUSED(LPR, NCH, CW)                                                                 \
+    do {                                                                                              \
+        if constexpr (CW == 8 || NCH <= 32)                                                           \
+            launch_ln_fwd<LPR, NCH, CW, true>(threads, grid, st, y16, mean, rstd, x16, g16, b16, r32, h32, eps, fz); \
+    } while (0)
 #define LS_LN_BWD(LPR, NCH, CW)                                                                 \
     do {                                                                                        \
         if (bl.lds_bytes > 65536 &&                                                             \
@@ -697,7 +752,7 @@ BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
                                 static_cast<int>(bl.lds_bytes)) != hipSuccess)                  \
             return fail(LS_ERR_HIP, "%s: cannot reserve %zu bytes of LDS", name, bl.lds_bytes); \
         launch_kernel(ln_bwd_kernel<LPR, NCH, CW>, dim3(bl.grid), dim3(bl.waves * kWave),         \
-                      bl.lds_bytes, st, dx16, part, dy16, x16, g16, mean, rstd, r32, h32);         \
+                      bl.lds_bytes, st, dx16, part, hdr, dy16, x16, g16, mean, rstd, r32, h32);    \
     } while (0)
 
 #define LS_LN_TABLE(M)                                                                          \
@@ -786,6 +841,20 @@ int ls_bias_dropout_residual_layernorm(void* z, void* y, float* mean, float* rst
                      aligned16(residual) && aligned16(gamma) && aligned16(beta);
     LnShape s;
     ln_shape(hidden, vec, &s);
+    if (s.cw == 1 && s.nch > 32) {
+        // Element-wise rows longer than 2048 do not fit the fused kernel's
+        // registers (x, residual, bias and each element's dropout words):
+        // the two standalone operators, one after the other, give the same
+        // bits.
+        int rc = ls_bias_dropout_residual(z, x, bias, residual, rows, hidden, p, seed, offset, stream);
+        if (rc != LS_OK) return rc;
+        rc = ls_layernorm_fwd(y, mean, rstd, z, gamma, beta, rows, hidden, eps, stream);
+        if (rc != LS_OK) return rc;
+        char buf[112];
+        snprintf(buf, sizeof(buf), "bias_dropout_residual_layernorm/two_launches_%s", s.name);
+        set_dispatch(buf);
+        return LS_OK;
+    }
     const int threads = fwd_threads(rows, s, true);
     const unsigned grid = fwd_grid(rows, s, threads);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -807,26 +876,27 @@ int ls_bias_dropout_residual_layernorm(void* z, void* y, float* mean, float* rst
 
 size_t ls_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
     if (rows <= 0 || hidden <= 0 || hidden > ls::kMaxHidden) return 0;
-    // Upper bound of the partial rows over every launch shape of (rows, hidden).
-    const int64_t blocks = rows < ls::kMaxBwdBlocks ? rows : ls::kMaxBwdBlocks;
-    return static_cast<size_t>(blocks) * 2 * static_cast<size_t>(hidden) * sizeof(float);
+    // A header (the partial-row count), then the partial rows: an upper bound
+    // over every launch shape of (rows, hidden).
+    return ls::kBwdHeaderBytes + static_cast<size_t>(ls::bwd_max_blocks(rows)) * 2 * static_cast<size_t>(hidden) *
+                                     sizeof(float);
 }
 
-int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
-                     const void* gamma, const float* mean, const float* rstd, int64_t rows,
-                     int64_t hidden, void* workspace, size_t workspace_bytes, void* stream) {
+int ls_layernorm_bwd_input(void* dx, const void* dy, const void* x, const void* gamma, const float* mean,
+                           const float* rstd, int64_t rows, int64_t hidden, void* workspace, size_t workspace_bytes,
+                           void* stream) {
     using namespace ls;
-    const char* name = "ls_layernorm_bwd";
+    const char* name = "ls_layernorm_bwd_input";
     if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
     if (rows == 0) {
         set_dispatch("empty");
-        return LS_OK;   // dgamma / dbeta of zero rows are left untouched
+        return LS_OK;
     }
     if (hidden == 0) return fail(LS_ERR_SHAPE, "%s: hidden must be >= 1", name);
     if (hidden > kMaxHidden)
         return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
     if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", name);   // 32-bit row loops
-    if (!dx || !dgamma || !dbeta || !dy || !x || !gamma || !mean || !rstd || !workspace)
+    if (!dx || !dy || !x || !gamma || !mean || !rstd || !workspace)
         return fail(LS_ERR_NULL, "%s: null pointer", name);
     const size_t need = ls_layernorm_bwd_workspace_bytes(rows, hidden);
     if (workspace_bytes < need)
@@ -841,20 +911,67 @@ int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const 
     auto* dy16 = static_cast<const half_t*>(dy);
     auto* x16 = static_cast<const half_t*>(x);
     auto* g16 = static_cast<const half_t*>(gamma);
-    auto* part = static_cast<float*>(workspace);
+    auto* hdr = static_cast<uint32_t*>(workspace);
+    auto* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kBwdHeaderBytes);
     const uint32_t r32 = static_cast<uint32_t>(rows), h32 = static_cast<uint32_t>(hidden);
     clear_hip_error();
     LS_LN_TABLE(LS_LN_BWD)
-    int rc = launch_status(name);
-    if (rc != LS_OK) return rc;
-    const unsigned fgrid = static_cast<unsigned>((2 * hidden + kFinCols - 1) / kFinCols);
-    ln_bwd_finalize_kernel<<<fgrid, kFinCols * kFinSlices, 0, st>>>(static_cast<half_t*>(dgamma),
-                                                                     static_cast<half_t*>(dbeta), part,
-                                                                     bl.grid, h32);
     char buf[96];
     snprintf(buf, sizeof(buf), "layernorm_bwd/%s_w%d_g%u", s.name, bl.waves, bl.grid);
     set_dispatch(buf);
     return launch_status(name);
+}
+
+int ls_layernorm_bwd_params(void* dgamma, void* dbeta, int64_t rows, int64_t hidden, const void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    using namespace ls;
+    const char* name = "ls_layernorm_bwd_params";
+    if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    if (hidden == 0) {
+        set_dispatch("empty");
+        return LS_OK;
+    }
+    if (hidden > kMaxHidden)
+        return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
+    if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", name);
+    if (!dgamma || !dbeta) return fail(LS_ERR_NULL, "%s: null pointer", name);
+    unsigned max_blocks = 0;
+    if (rows > 0) {
+        if (!workspace) return fail(LS_ERR_NULL, "%s: null workspace", name);
+        const size_t need = ls_layernorm_bwd_workspace_bytes(rows, hidden);
+        if (workspace_bytes < need)
+            return fail(LS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", name, workspace_bytes, need);
+        if (!aligned16(workspace)) return fail(LS_ERR_PARAM, "%s: workspace must be 16-byte aligned", name);
+        max_blocks = bwd_max_blocks(rows);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint32_t h32 = static_cast<uint32_t>(hidden);
+    const auto* ws = static_cast<const char*>(workspace);
+    clear_hip_error();
+    const unsigned fgrid = static_cast<unsigned>((2 * hidden + kFinCols - 1) / kFinCols);
+    launch_kernel(ln_bwd_finalize_kernel, dim3(fgrid), dim3(kFinCols * kFinSlices), 0, st,
+                  static_cast<half_t*>(dgamma), static_cast<half_t*>(dbeta), reinterpret_cast<const uint32_t*>(ws),
+                  reinterpret_cast<const float*>(ws ? ws + kBwdHeaderBytes : nullptr), max_blocks, h32);
+    set_dispatch(rows > 0 ? "layernorm_bwd_params/fixed_order" : "layernorm_bwd_params/zero_rows");
+    return launch_status(name);
+}
+
+int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
+                     const void* gamma, const float* mean, const float* rstd, int64_t rows,
+                     int64_t hidden, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* name = "ls_layernorm_bwd";
+    if (rows < 0 || hidden < 0) return ls::fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    if (rows > 0) {
+        const int rc = ls_layernorm_bwd_input(dx, dy, x, gamma, mean, rstd, rows, hidden, workspace,
+                                              workspace_bytes, stream);
+        if (rc != LS_OK) return rc;
+    }
+    char disp[128];
+    snprintf(disp, sizeof(disp), "%s", ls_last_dispatch());
+    const int rc = ls_layernorm_bwd_params(dgamma, dbeta, rows, hidden, workspace, workspace_bytes, stream);
+    if (rc != LS_OK) return rc;
+    ls::set_dispatch(rows > 0 ? disp : "layernorm_bwd/zero_rows");
+    return LS_OK;
 }
 
 }  // extern "C"

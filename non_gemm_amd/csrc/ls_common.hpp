@@ -266,10 +266,20 @@ __device__ __forceinline__ void unpack8(const half8 h, float f[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) f[j] = static_cast<float>(h[j]);
 }
+// fp32 -> fp16, round to nearest even, always from the fp32 value: the
+// empty asm statement hides the value's origin, so the compiler cannot fold
+// the conversion into the fma that produced it (v_fma_mix*_f16 rounds the
+// exact product-sum straight to fp16, which can differ by one ulp from
+// rounding the fp32 result, and whether it is chosen varies between
+// instantiations of the same source).
+__device__ __forceinline__ half_t to_half(float v) {
+    asm("" : "+v"(v));
+    return static_cast<half_t>(v);
+}
 __device__ __forceinline__ half8 pack8(const float f[8]) {
     half8 h;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = static_cast<half_t>(f[j]);   // round to nearest even
+    for (int j = 0; j < 8; ++j) h[j] = to_half(f[j]);
     return h;
 }
 

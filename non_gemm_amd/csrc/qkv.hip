@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kBlock) void qkv_split_scalar_kernel(half_t* out, c
         const uint64_t k = c / hid, h = (c % hid) / d, j = c % d;
         const uint64_t b = t / seq, l = t % seq;
         const float y = static_cast<float>(qkv[i]) + static_cast<float>(bias[c]);
-        out[(((k * batch + b) * heads + h) * seq + l) * d + j] = static_cast<half_t>(y);
+        out[(((k * batch + b) * heads + h) * seq + l) * d + j] = to_half(y);
     }
 }
 

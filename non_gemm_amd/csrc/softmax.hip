@@ -61,7 +61,7 @@ struct Chunk<1> {
         f[0] = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(r)));
     }
     static __device__ __forceinline__ void store(half_t* p, size_t i, const float f[1]) {
-        p[i] = static_cast<half_t>(f[0]);
+        p[i] = to_half(f[0]);
     }
 };
 

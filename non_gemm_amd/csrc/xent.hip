@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kBlock) void xent_bwd_scalar_kernel(half_t* dx, con
             const bool bad = y < 0 || static_cast<uint32_t>(y) >= a.vocab;
             o = xent_grad(static_cast<float>(logits[i]), lse[row], j, y, bad, g, a);
         }
-        dx[i] = static_cast<half_t>(o);
+        dx[i] = to_half(o);
     }
 }
 

@@ -261,6 +261,32 @@ def layernorm_bwd(dy, x, gamma, mean, rstd, dx=None, dgamma=None, dbeta=None, wo
     return dx, dgamma, dbeta
 
 
+def layernorm_bwd_input(dy, x, gamma, mean, rstd, workspace, dx=None):
+    """First half of layernorm_bwd: dx, and the dgamma / dbeta partials in
+    `workspace` (uint8, at least layernorm_bwd_workspace_bytes).  Returns dx."""
+    _dev(dy, x, gamma, mean, rstd, dx, workspace)
+    rows, h = _rows_cols(x)
+    if dy.shape != x.shape or gamma.shape != (h,) or mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("shape mismatch")
+    dx = torch.empty_like(x) if dx is None else dx
+    check("ls_layernorm_bwd_input", load().ls_layernorm_bwd_input(
+        _ptr(dx), _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), rows, h, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return dx
+
+
+def layernorm_bwd_params(rows, hidden, workspace, dgamma=None, dbeta=None, device="cuda"):
+    """Second half of layernorm_bwd: dgamma, dbeta from the partials of the
+    matching layernorm_bwd_input call.  Returns (dgamma, dbeta)."""
+    _dev(workspace, dgamma, dbeta)
+    dgamma = torch.empty(hidden, dtype=_F16, device=device) if dgamma is None else dgamma
+    dbeta = torch.empty(hidden, dtype=_F16, device=device) if dbeta is None else dbeta
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("ls_layernorm_bwd_params", load().ls_layernorm_bwd_params(
+        _ptr(dgamma), _ptr(dbeta), int(rows), int(hidden), _ptr(workspace), nbytes, _stream()))
+    return dgamma, dbeta
+
+
 def softmax_fwd(x, key_lengths=None, causal=False, y=None):
     """x [batch, heads, q_len, k_len] fp16; key_lengths int32 [batch] or None."""
     _dev(x, key_lengths, y)

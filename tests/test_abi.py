@@ -78,7 +78,8 @@ def test_layernorm_validation(lib):
     assert lib.ls_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 31, 8,
                                 FAKE, 1 << 40, s) == LS_ERR_SHAPE
     need = lib.ls_layernorm_bwd_workspace_bytes(4096, 768)
-    assert need > 0 and need % (2 * 768 * 4) == 0
+    assert need == 256 + 256 * 2 * 768 * 4          # header, then at most 256 partial rows of 2H floats
+    assert lib.ls_layernorm_bwd_workspace_bytes(5, 768) == 256 + 5 * 2 * 768 * 4
     assert lib.ls_layernorm_bwd_workspace_bytes(0, 768) == 0
     assert lib.ls_layernorm_bwd_workspace_bytes(10, 5000) == 0
     assert lib.ls_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 768,
@@ -87,6 +88,19 @@ def test_layernorm_validation(lib):
                                 None, need, s) == LS_ERR_NULL
     assert lib.ls_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 768,
                                 ctypes.c_void_p(0x1008), need, s) == LS_ERR_PARAM
+    # the two halves validate the same way; nothing is launched on these paths
+    assert lib.ls_layernorm_bwd_input(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 768, FAKE, need - 1,
+                                      s) == LS_ERR_WORKSPACE
+    assert lib.ls_layernorm_bwd_input(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4096, 768, FAKE, need, s) == LS_ERR_NULL
+    assert lib.ls_layernorm_bwd_input(None, None, None, None, None, None, 0, 768, None, 0, s) == LS_OK
+    assert lib.ls_layernorm_bwd_params(FAKE, FAKE, 4096, 768, FAKE, need - 1, s) == LS_ERR_WORKSPACE
+    assert lib.ls_layernorm_bwd_params(FAKE, FAKE, 4096, 768, None, need, s) == LS_ERR_NULL
+    assert lib.ls_layernorm_bwd_params(None, FAKE, 0, 768, None, 0, s) == LS_ERR_NULL
+    assert lib.ls_layernorm_bwd_params(FAKE, FAKE, 4096, 5000, FAKE, need, s) == LS_ERR_UNSUPPORTED
+    assert lib.ls_layernorm_bwd_params(FAKE, FAKE, -1, 768, FAKE, need, s) == LS_ERR_SHAPE
+    assert lib.ls_layernorm_bwd_params(FAKE, FAKE, 4096, 768, ctypes.c_void_p(0x1008), need, s) == LS_ERR_PARAM
+    # rows == 0: the zero-row sums still need their outputs
+    assert lib.ls_layernorm_bwd(None, None, FAKE, None, None, None, None, None, 0, 768, None, 0, s) == LS_ERR_NULL
 
 
 def test_softmax_validation(lib):

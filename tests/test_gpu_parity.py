@@ -445,6 +445,14 @@ def test_layernorm_offset_rows(ls, rows, h):
     assert_fp16(host(db), rdb, tag + " dbeta")
 
 
+def assert_fused_z(z, rz, tag):
+    """The stored sum: the fp16 bar, and at most one element in 1000 rounded
+    differently from the oracle at all (midpoint cases of the fp32 sum)."""
+    assert_fp16(z, rz, tag + " z")
+    differ = np.count_nonzero(np.asarray(z).view(np.uint16) != np.asarray(rz).view(np.uint16))
+    assert differ <= max(1, np.asarray(z).size // 1000), f"{tag}: {differ} elements of z round differently"
+
+
 FUSED_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (77, 96), (33, 512), (9, 1536), (3, 4096), (20, 13),
                 (1030, 767), (5, 2048), (300, 768), (1, 8), (16384, 256), (4, 4095)]
 
@@ -462,8 +470,13 @@ def test_bias_dropout_residual_layernorm(ls, rows, h, p):
     z, y, mean, rstd = ls.bias_dropout_residual_layernorm(dev(x), dev(b), dev(r), dev(gamma), dev(beta), p, SEED,
                                                           off, eps)
     tag = f"bias_dropout_residual_layernorm {rows}x{h} p={p} [{last_dispatch()}]"
-    rz, ry, rmean, rrstd = oracle.bias_dropout_residual_layernorm(x, b, r, gamma, beta, p, SEED, off, BITS, eps)
-    assert_fp16(host(z), rz, tag + " z")
+    rz, _, _, _ = oracle.bias_dropout_residual_layernorm(x, b, r, gamma, beta, p, SEED, off, BITS, eps)
+    assert_fused_z(host(z), rz, tag)
+    # An fp32 sum within 2^-24 of an fp16 rounding midpoint can round the
+    # other way from the oracle's float64 sum (one element in ~4000): y and
+    # the statistics are held to their bars against the oracle's LayerNorm of
+    # the stored z, which is what the kernel normalises.
+    ry, rmean, rrstd = oracle.layernorm_fwd(host(z), gamma, beta, eps)
     assert_fp16(host(y), ry, tag + " y")
     sigma = 1.0 / rrstd.astype(np.float64)
     assert_fp32(host(mean), rmean, tag + " mean", floor=sigma)
@@ -486,8 +499,7 @@ def test_bias_dropout_residual_layernorm_aliasing_offsets_and_empty(ls):
     r = synth.offset_rows16(g, rows, h)
     b = synth.normal16(g, (h,), 0.02)
     gamma, beta = synth.uniform16(g, (h,), 0.5, 1.5), synth.normal16(g, (h,), 0.1)
-    rz, ry, rmean, rrstd = oracle.bias_dropout_residual_layernorm(x, b, r, gamma, beta, p, SEED, 2, BITS, eps)
-    sigma = 1.0 / rrstd.astype(np.float64)
+    rz, _, _, _ = oracle.bias_dropout_residual_layernorm(x, b, r, gamma, beta, p, SEED, 2, BITS, eps)
     for target in ("residual", "x"):
         xt, rt = dev(x), dev(r)
         zt = rt if target == "residual" else xt
@@ -495,8 +507,10 @@ def test_bias_dropout_residual_layernorm_aliasing_offsets_and_empty(ls):
                                                               eps, z=zt)
         tag = f"fused, z aliasing {target} [{last_dispatch()}]"
         assert z.data_ptr() == zt.data_ptr()
-        assert_fp16(host(z), rz, tag + " z")
+        assert_fused_z(host(z), rz, tag)
+        ry, rmean, rrstd = oracle.layernorm_fwd(host(z), gamma, beta, eps)     # LayerNorm of the stored z
         assert_fp16(host(y), ry, tag + " y")
+        sigma = 1.0 / rrstd.astype(np.float64)
         assert_fp32(host(mean), rmean, tag + " mean", floor=sigma)
         assert_fp32(host(rstd), rrstd, tag + " rstd")
     e = torch.empty((0, h), dtype=torch.float16, device="cuda")
@@ -510,6 +524,55 @@ def test_bias_dropout_residual_layernorm_aliasing_offsets_and_empty(ls):
                                                     t.data_ptr(), t.data_ptr(), t.data_ptr(), t.data_ptr(),
                                                     t.data_ptr(), rows, h, bad_p, SEED, 2, bad_eps, S)
         assert rc == 3      # LS_ERR_PARAM
+
+
+@pytest.mark.parametrize("rows,h,offset", [(4096, 768, 0), (300, 768, 1), (77, 96, 0), (5, 2048, 1), (1030, 767, 0),
+                                           (8192, 1024, 0)])
+def test_layernorm_bwd_split_calls(ls, rows, h, offset):
+    """ls_layernorm_bwd_input then ls_layernorm_bwd_params, the second on
+    another stream ordered by an event, give the combined call's results bit
+    for bit (offset 1: dx one element into its buffer, so the element-wise
+    path runs, whose block count differs from the vector path's)."""
+    x, gamma, beta, dy = ln_inputs(rows, h, rows + 5 * h)
+    _, mean, rstd = oracle.layernorm_fwd(x, gamma, beta, synth.LN_EPS)
+    args = (dev(dy), dev(x), dev(gamma), dev(mean), dev(rstd))
+    dxbuf = torch.empty(rows * h + offset, dtype=torch.float16, device="cuda")
+    dx_full = dxbuf[offset:].view(rows, h)
+    ref = ls.layernorm_bwd(*args, dx=dx_full)
+    ref = [host(t).copy() for t in ref]
+    ws = torch.empty(ls.layernorm_bwd_workspace_bytes(rows, h), dtype=torch.uint8, device="cuda")
+    dxbuf2 = torch.empty_like(dxbuf)
+    dx = ls.layernorm_bwd_input(*args, ws, dx=dxbuf2[offset:].view(rows, h))
+    tag = f"layernorm_bwd split {rows}x{h} [{last_dispatch()}]"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dg, db = ls.layernorm_bwd_params(rows, h, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for a, b, what in ((dx, ref[0], "dx"), (dg, ref[1], "dgamma"), (db, ref[2], "dbeta")):
+        assert np.array_equal(host(a).view(np.uint16), b.view(np.uint16)), f"{tag}: {what}"
+
+
+def test_layernorm_bwd_zero_rows_and_stale_header(ls):
+    """No rows: dgamma and dbeta are the sums over no rows, zeros, from the
+    combined call and from the parameter call alone (no workspace).  A
+    workspace whose header no input call wrote: the count is clamped to what
+    the workspace holds, so the call reads inside it (values unspecified)."""
+    h = 768
+    for call in ("combined", "params"):
+        dg = torch.full((h,), 7.0, dtype=torch.float16, device="cuda")
+        db = torch.full((h,), -7.0, dtype=torch.float16, device="cuda")
+        if call == "combined":
+            e = torch.empty((0, h), dtype=torch.float16, device="cuda")
+            ls.layernorm_bwd(e, e, dev(np.ones(h, np.float16)), torch.empty(0, device="cuda"),
+                             torch.empty(0, device="cuda"), dgamma=dg, dbeta=db)
+        else:
+            ls.layernorm_bwd_params(0, h, None, dgamma=dg, dbeta=db)
+        assert np.all(host(dg) == 0) and np.all(host(db) == 0), call
+    rows = 64
+    ws = torch.full((ls.layernorm_bwd_workspace_bytes(rows, h),), 0x7F, dtype=torch.uint8, device="cuda")
+    ls.layernorm_bwd_params(rows, h, ws)
+    torch.cuda.synchronize()
 
 
 def test_layernorm_bwd_workspace_reuse(ls):
