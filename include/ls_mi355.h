@@ -314,9 +314,11 @@ int ls_embedding_fwd(void* out, const int32_t* ids, const void* tok_emb, const v
 /* Embedding backward ([LS2] sec. 2.1.2): for every token t with id w,
  *     grad_tok_emb[w, c] += scale * keep(t*hidden + c) / (1-p_eff) * dy[t, c]
  * Repeated ids collide on one row of the table; the collisions are summed
- * with fp32 atomic adds, after the repeats inside each chunk of 64 tokens
- * have been added up in registers.  The atomics' order is not fixed, so two
- * runs agree to fp32 rounding, not bit for bit.
+ * with fp32 atomic adds, after the repeats inside each chunk of tokens have
+ * been added up in registers: each block sorts the (id, position) keys of a
+ * 1024-token chunk (64-token chunks, sorted by one wave, when vocab >= 2^22).
+ * The atomics' order is not fixed, so two runs agree to fp32 rounding, not
+ * bit for bit.
  * grad_tok_emb: fp32 [vocab, hidden]; if zero_first != 0 it is zeroed first
  * (by a fill kernel on the same stream), otherwise the call accumulates.
  * dy: fp16 [batch*seq_len, hidden].  (seed, offset, p) must be those of the
@@ -374,17 +376,23 @@ int ls_probe_copy(void* dst, const void* src, int64_t bytes, void* stream);
 int ls_probe_read(float* sink, const void* src, int64_t bytes, void* stream);
 
 /* Kernel timing hook.  Arms two HIP events (hipEvent_t passed as void*) for
- * the calling thread: the next call of ls_bias_dropout_residual,
- * ls_bias_relu_dropout or ls_layernorm_bwd (its row kernel, not the column
- * sums after it) launches that kernel with hipExtLaunchKernel, which records
- * start_event when the kernel begins and stop_event when it ends, on the
- * call's stream; then the events are disarmed.  hipEventElapsedTime(start,
+ * the calling thread's next operator call: if that call's first kernel is
+ * launched through the hook (ls_bias_dropout_residual, ls_bias_relu_dropout,
+ * ls_layernorm_fwd, ls_bias_dropout_residual_layernorm, ls_layernorm_bwd and
+ * ls_layernorm_bwd_input: their row kernel), the launch goes through
+ * hipExtLaunchKernel, which records start_event when the kernel begins and
+ * stop_event when it ends, on the call's stream.  hipEventElapsedTime(start,
  * stop) is then the kernel's own duration, without the command processor's
- * handling of separate event records.  The library neither creates, waits
- * on nor destroys the events.  Calls of other operators, and calls that
- * return an error before launching, leave the armed events in place.  A NULL
- * event disarms and returns LS_ERR_NULL. */
+ * handling of separate event records.  Whatever that next call does -- a
+ * timed launch, another launch, no launch, or an error -- the events are
+ * disarmed when it returns, so they can never attach to a later, unrelated
+ * kernel.  The library neither creates, waits on nor destroys the events.
+ * A NULL event disarms and returns LS_ERR_NULL. */
 int ls_time_next_launch(void* start_event, void* stop_event);
+
+/* 1 while a pair of timing events is armed for the calling thread, else 0
+ * (introspection for tests). */
+int ls_time_armed(void);
 
 /* Width in bits of the random field behind one dropout decision (16). */
 int ls_dropout_decision_bits(void);
@@ -396,7 +404,8 @@ const char* ls_status_string(int status);
 const char* ls_last_error(void);
 
 /* Thread-local name of the kernel specialisation the last successful call on
- * this thread launched (e.g. "layernorm_fwd/lpr32_vpl3"). */
+ * this thread launched (e.g. "layernorm_fwd/lpr64_nch2_v8_b1024": 64 lanes
+ * per row, 2 chunks of 8 fp16 per lane, 1024-thread blocks). */
 const char* ls_last_dispatch(void);
 
 /* Library version string. */

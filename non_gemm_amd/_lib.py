@@ -65,6 +65,7 @@ SIGNATURES = {
     "ls_probe_copy": (c_int, [c_void_p, c_void_p, c_i64, c_void_p]),
     "ls_probe_read": (c_int, [c_void_p, c_void_p, c_i64, c_void_p]),
     "ls_time_next_launch": (c_int, [c_void_p, c_void_p]),
+    "ls_time_armed": (c_int, []),
     "ls_dropout_decision_bits": (c_int, []),
     "ls_status_string": (ctypes.c_char_p, [c_int]),
     "ls_last_error": (ctypes.c_char_p, []),

@@ -15,7 +15,12 @@ thread_local hipEvent_t g_time_stop = nullptr;
 
 namespace ls {
 
+// Armed timing events live for one operator call: every call ends through
+// fail(), launch_status() or set_dispatch(), and each of them disarms.
+static void disarm() { g_time_start = g_time_stop = nullptr; }
+
 int fail(int status, const char* fmt, ...) {
+    disarm();
     va_list ap;
     va_start(ap, fmt);
     std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
@@ -24,6 +29,7 @@ int fail(int status, const char* fmt, ...) {
 }
 
 void set_dispatch(const char* name) {
+    disarm();
     std::snprintf(g_last_dispatch, sizeof(g_last_dispatch), "%s", name);
 }
 
@@ -38,6 +44,7 @@ bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
 }
 
 int launch_status(const char* what) {
+    disarm();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(LS_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
@@ -72,6 +79,8 @@ int ls_time_next_launch(void* start_event, void* stop_event) {
     g_time_stop = static_cast<hipEvent_t>(stop_event);
     return LS_OK;
 }
+
+int ls_time_armed(void) { return g_time_start != nullptr ? 1 : 0; }
 
 const char* ls_last_error(void) { return g_last_error; }
 const char* ls_last_dispatch(void) { return g_last_dispatch; }

@@ -174,7 +174,7 @@ extern "C" int ls_adam_workspace_step(void* param, const void* grad, float* exp_
             adam_kernel<true><<<static_cast<unsigned>(blocks), kBlock, 0, st>>>(p16, g16, exp_avg, exp_avg_sq, un, n4, a);
         else
             adam_kernel<false><<<static_cast<unsigned>(blocks), kBlock, 0, st>>>(p16, g16, exp_avg, exp_avg_sq, un, n4, a);
-        set_dispatch(decoupled_wd ? "adam/vec8_adamw" : "adam/vec8_l2");
+        set_dispatch(decoupled_wd ? "adam/groups4x4_adamw" : "adam/groups4x4_l2");
     } else {
         uint64_t blocks = (un + kBlock - 1) / kBlock;
         if (blocks > 65536) blocks = 65536;

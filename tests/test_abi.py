@@ -27,6 +27,11 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
+    # LS_MI355_TEST_LIB: another build of the same library (the host-sanitized
+    # one, run by test_abi_sanitized.py)
+    other = os.environ.get("LS_MI355_TEST_LIB")
+    if other:
+        return _lib.load(other)
     if not os.path.exists(_lib.LIB_PATH):
         from non_gemm_amd import build
         build.build()
@@ -219,3 +224,22 @@ def test_time_next_launch_validation(lib):
     assert lib.ls_time_next_launch(None, FAKE) == LS_ERR_NULL
     assert lib.ls_time_next_launch(FAKE, None) == LS_ERR_NULL
     assert b"null event" in lib.ls_last_error()
+
+
+def test_timing_events_last_one_operator_call(lib):
+    """Armed events belong to the next operator call, whatever it does: a
+    call rejected before launching, or one with nothing to launch, disarms
+    them, so they never attach to a later, unrelated kernel."""
+    s = None
+    assert lib.ls_time_next_launch(FAKE, FAKE) == LS_OK and lib.ls_time_armed() == 1
+    lib.ls_layernorm_bwd_workspace_bytes(8, 8)                     # a size query is not an operator call
+    assert lib.ls_time_armed() == 1
+    assert lib.ls_layernorm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 0.0, s) == LS_ERR_PARAM
+    assert lib.ls_time_armed() == 0
+    assert lib.ls_time_next_launch(FAKE, FAKE) == LS_OK
+    assert lib.ls_bias_relu_dropout(None, None, None, 0, 8, 0.1, 1, 0, s) == LS_OK      # empty: no launch
+    assert lib.ls_time_armed() == 0
+    assert lib.ls_time_next_launch(FAKE, FAKE) == LS_OK
+    assert lib.ls_softmax_bwd(FAKE, None, FAKE, 4, 128, s) == LS_ERR_NULL               # not a hooked operator
+    assert lib.ls_time_armed() == 0
+    assert lib.ls_time_next_launch(None, FAKE) == LS_ERR_NULL and lib.ls_time_armed() == 0
