@@ -1174,8 +1174,7 @@ def test_timed_launch_same_result_and_events(ls):
     out2 = ls.bias_relu_dropout(x, b, 0.1, SEED, 1)        # disarmed: plain launch
     assert np.array_equal(host(out2).view(np.uint16), ref.view(np.uint16))
 
-    # the LayerNorm backward's row kernel takes the same hook; a call that
-    # fails validation before launching leaves the events armed for it
+    # the LayerNorm backward's row kernel takes the same hook
     xs, gamma, beta, dy = ln_inputs(4096, 768, 5)
     _, mean, rstd = oracle.layernorm_fwd(xs, gamma, beta, synth.LN_EPS)
     args = (dev(dy), dev(xs), dev(gamma), dev(mean), dev(rstd))
@@ -1185,13 +1184,20 @@ def test_timed_launch_same_result_and_events(ls):
     f1.record()
     torch.cuda.synchronize()
     assert lib.ls_time_next_launch(f0.cuda_event, f1.cuda_event) == 0
-    with pytest.raises(_lib.LsError):
-        ls.layernorm_fwd(dev(xs), dev(gamma), dev(beta), 0.0)       # eps <= 0: rejected, nothing launched
     got = [host(t) for t in ls.layernorm_bwd(*args)]
     torch.cuda.synchronize()
     for a_, b_ in zip(got, ref_ln):
         assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
     assert 0.0 < f0.elapsed_time(f1) < 10.0
+    # a call rejected before launching disarms the events: the next call runs
+    # untimed
+    assert lib.ls_time_next_launch(f0.cuda_event, f1.cuda_event) == 0 and lib.ls_time_armed() == 1
+    with pytest.raises(_lib.LsError):
+        ls.layernorm_fwd(dev(xs), dev(gamma), dev(beta), 0.0)       # eps <= 0: rejected, nothing launched
+    assert lib.ls_time_armed() == 0
+    got = [host(t) for t in ls.layernorm_bwd(*args)]
+    for a_, b_ in zip(got, ref_ln):
+        assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
 
 
 @pytest.mark.parametrize("k", [16384, 65536])
