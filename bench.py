@@ -639,6 +639,24 @@ def extra_rows(torch, ops):
     us_s = a.elapsed_time(b) / 40 * 1e3
     out["adam_workspace_shard"] = row(f"{n8 / 1e6:.2f}M params (350M sharded 8 ways by range), 1 launch", us_s,
                                       22 * n8, params_per_s=round(n8 / us_s * 1e6, 1))
+
+    # The ten steps of the Adam workload from zero moments, and after each
+    # the share of fp16 parameters the step left bit-identical: with no fp32
+    # master copy an update below half an fp16 spacing of the parameter is
+    # lost, which is the trainer's cost in accuracy.
+    gen.manual_seed(5)
+    prm.copy_((torch.randn(n, device="cuda", generator=gen) * 0.02).half())
+    m.zero_()
+    v.zero_()
+    prev = prm.clone()
+    unchanged = []
+    for st in range(1, synth.ADAM_STEPS + 1):
+        ops.adam_workspace_step(prm, grd, m, v, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                hp["weight_decay"], st, hp["grad_scale"], hp["decoupled_wd"])
+        unchanged.append(round((prm == prev).sum().item() / n, 7))
+        prev.copy_(prm)
+    out["adam_workspace_step"]["unchanged_fraction_per_step"] = unchanged
+    del prev
     del prm, grd, m, v
     torch.cuda.empty_cache()
     return out
@@ -1010,6 +1028,28 @@ def main():
         us = a.elapsed_time(b) * 1e3 / (reps * len(sets) * counts[name])
         kernels[name] = {"us": round(us, 2), "bytes": per[name], "GB/s": round(per[name] / us / 1e3, 1),
                          "per_step": counts[name]}
+    # The Philox rounds' cost: bias+ReLU+dropout (the lowest bytes per
+    # decision of the chain) at p = 0, which skips the rounds, against p = 0.1.
+    philox = None
+    if "bias_relu_dropout" in kernels:
+        items = []
+        for s in sets:
+            for it in s.launches:
+                if it[0] == "bias_relu_dropout":
+                    a = list(it[3])
+                    a[5] = 0.0                                   # p
+                    items.append((it[0], it[1], it[2], tuple(a)))
+        g0 = capture_items(torch, items, cap_stream, check, None)
+        us0 = replay_us(torch, [g0], 20) / len(items)
+        us1 = kernels["bias_relu_dropout"]["us"]
+        elems = shape.tokens * shape.ffn
+        philox = {"kernel": f"bias_relu_dropout [{shape.tokens},{shape.ffn}]", "us_p0.1": us1, "us_p0": round(us0, 2),
+                  "extra_us": round(us1 - us0, 2), "extra_ns_per_element": round((us1 - us0) * 1e3 / elems, 6),
+                  "share_of_kernel": round((us1 - us0) / us1, 4),
+                  # from the generated code: per call of 8 decisions, 20 v_mad_u64_u32 and 20 v_bitop3_b32
+                  # (ten rounds, two products and two three-way XORs each), then 8 compares and selects
+                  "valu_instructions_per_element": (20 + 20 + 16) / 8}
+        del g0
     # The largest single launch, from the same cold graph timing (not live events).
     largest = None
     if LARGEST in kernels:
@@ -1072,6 +1112,7 @@ def main():
                          "achieved": kernels[DOMINANT]["GB/s"],
                          "frac": round(kernels[DOMINANT]["GB/s"] / HBM_PEAK_GBPS, 4)}},
         "roofline_largest_launch": largest,
+        "philox_cost": philox,
         "cpu_baseline": cpu,
         "kernels_cold": kernels,
         "warm_chain_us": None if warm_us is None else round(warm_us, 2),

@@ -811,6 +811,31 @@ def test_embedding_invalid_ids(ls):
 # Adam over the workspace
 # ----------------------------------------------------------------------------
 
+def fp16_ulp(x):
+    """Spacing of fp16 numbers at x (subnormal spacing below 2^-14)."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def assert_adam_update(p_gpu, p_ref, p0, tag, ulps=2):
+    """The update itself, p - p0, against the oracle's: within `ulps` fp16
+    spacings of the parameter (each step rounds p to fp16; fp32 and float64
+    arithmetic may round a step differently now and then).  A step that is
+    missing, halved, doubled or of the wrong sign moves p by many spacings
+    (lr = 1e-4 is ~6 spacings at |p| = 0.02 per step) and fails."""
+    d_gpu = np.asarray(p_gpu, np.float64) - np.asarray(p0, np.float64)
+    d_ref = np.asarray(p_ref, np.float64) - np.asarray(p0, np.float64)
+    tol = ulps * fp16_ulp(np.maximum(np.abs(np.asarray(p_ref, np.float64)), np.abs(np.asarray(p0, np.float64))))
+    bad = ~(np.abs(d_gpu - d_ref) <= tol)
+    if bad.any():
+        i = int(np.argwhere(bad)[0][0])
+        raise AssertionError(f"{tag}: update of {int(bad.sum())}/{bad.size} parameters off by more than {ulps} "
+                             f"fp16 spacings; first at {i}: {d_gpu[i]} vs oracle {d_ref[i]} (p0 {p0[i]})")
+    moved = np.count_nonzero(d_ref)
+    assert moved == 0 or np.count_nonzero(d_gpu) >= 0.9 * moved, f"{tag}: parameters left unchanged"
+
+
 @pytest.mark.parametrize("n,decoupled,offset,steps", [(1_000_003, True, 0, 10), (77, True, 0, 10),
                                                       (50_001, True, 3, 10), (4096, False, 0, 1),
                                                       (4096, False, 0, 10), (2052, True, 0, 3)])
@@ -840,9 +865,34 @@ def test_adam_steps(ls, n, decoupled, offset, steps):
                                                 decoupled)
     tag = f"adam n={n} steps={steps} [{last_dispatch()}]"
     assert_fp16(host(pt), rp, tag + " param")
+    assert_adam_update(host(pt), rp, p, tag)
     if decoupled or steps == 1:
         assert_fp32(host(mt), rm, tag + " exp_avg")
         assert_fp32(host(vt), rv, tag + " exp_avg_sq")
+
+
+@pytest.mark.parametrize("decoupled", [True, False])
+def test_adam_large_steps(ls, decoupled):
+    """lr 1e-2 and weight decay 0.1: every step moves a parameter by far more
+    than the fp16 bar, so the parameter values themselves pin the update
+    (sign, size, bias corrections, the weight-decay form) over ten steps."""
+    n = 20_011
+    g = np.random.default_rng(77 + decoupled)
+    p = synth.normal16(g, (n,), 0.5)
+    gr = synth.normal16(g, (n,), 1e-2)
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.98, eps=1e-8, weight_decay=0.1, grad_scale=1.0)
+    pt, gt = dev(p), dev(gr)
+    mt, vt = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    rp, rm, rv = p, np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for step in range(1, 11):
+        ls.adam_workspace_step(pt, gt, mt, vt, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
+                               step, hp["grad_scale"], decoupled)
+        rp, rm, rv = oracle.adam_workspace_step(rp, gr, rm, rv, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                                hp["weight_decay"], step, hp["grad_scale"], decoupled)
+    tag = f"adam lr 1e-2 decoupled={decoupled} [{last_dispatch()}]"
+    assert_fp16(host(pt), rp, tag + " param")
+    assert_adam_update(host(pt), rp, p, tag)
+    assert np.mean(np.abs(rp.astype(np.float64) - p.astype(np.float64)) > 0.05) > 0.9     # the steps are large
 
 
 def test_adam_full_workspace_sampled(ls):
@@ -872,6 +922,7 @@ def test_adam_full_workspace_sampled(ls):
     ti = torch.from_numpy(idx).cuda()
     tag = f"adam 350M sampled [{last_dispatch()}]"
     assert_fp16(host(pt[ti]), rp, tag + " param")
+    assert_adam_update(host(pt[ti]), rp, p[idx], tag)
     assert_fp32(host(mt[ti]), rm, tag + " exp_avg")
     assert_fp32(host(vt[ti]), rv, tag + " exp_avg_sq")
 
