@@ -261,6 +261,24 @@ int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const 
                      const void* gamma, const float* mean, const float* rstd, int64_t rows,
                      int64_t hidden, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ls_layernorm_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the header and partial rows live in a
+ * file-scope device array of ls_layernorm_bwd_noalloc_max_bytes() bytes
+ * (256 + 2 MiB), one copy per GPU, held until the process ends.  The call
+ * allocates and frees nothing.  Shapes whose ls_layernorm_bwd_workspace_bytes
+ * exceed that size (hidden > 1024 with more than 2^18 / hidden rows) return
+ * LS_ERR_WORKSPACE before launching.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, different
+ * host threads) race and give undefined results; calls ordered on one
+ * stream are safe (nothing in the array needs clearing between calls: each
+ * call writes what it later reads).  Otherwise exactly ls_layernorm_bwd:
+ * same arguments minus the workspace, same results, same errors. */
+size_t ls_layernorm_bwd_noalloc_max_bytes(void);
+int ls_layernorm_bwd_noalloc(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
+                             const void* gamma, const float* mean, const float* rstd, int64_t rows,
+                             int64_t hidden, void* stream);
+
 /* The two halves of ls_layernorm_bwd, for callers that keep the parameter
  * gradients off the critical path: only the input gradient dx feeds the
  * rest of the backward pass, while dgamma / dbeta wait for the optimizer, so

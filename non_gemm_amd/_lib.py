@@ -49,6 +49,9 @@ SIGNATURES = {
     "ls_layernorm_bwd_workspace_bytes": (c_size, [c_i64, c_i64]),
     "ls_layernorm_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_size, c_void_p]),
+    "ls_layernorm_bwd_noalloc_max_bytes": (c_size, []),
+    "ls_layernorm_bwd_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_i64, c_i64, c_void_p]),
     "ls_layernorm_bwd_input": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64,
                                        c_void_p, c_size, c_void_p]),
     "ls_layernorm_bwd_params": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_size, c_void_p]),

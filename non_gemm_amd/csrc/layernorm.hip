@@ -19,6 +19,7 @@
 // per chunk; CW = 1: the element-wise path for unaligned rows).  Chunk j of
 // lane l starts at column (l + j*LPR)*CW, so at every j the LPR lanes of a
 // row read one contiguous span.
+#include <mutex>
 #include <type_traits>
 
 #include "ls_common.hpp"
@@ -776,6 +777,40 @@ BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
         }                                                                                       \
     }
 
+// ---------------------------------------------------------------------------
+// Allocation-free LayerNorm backward: the workspace (header + partial rows)
+// lives in a file-scope device array, one copy per GPU, held until the
+// process ends.  2 MiB of partial rows cover hidden <= 1024 at any row count
+// (at most 256 partial rows of 2 * hidden floats), and wider rows while
+// rows * 2 * hidden * 4 bytes fit.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = kBwdHeaderBytes + (size_t(2) << 20);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's copy of `scratch`, looked up once per
+// device with that device current (in host code the array's name is only a
+// stand-in for the symbol, never passed to a kernel or a copy).
+int scratch_for_current_device(const char* name, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(LS_ERR_HIP, "%s: hipGetDevice failed", name);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(LS_ERR_UNSUPPORTED, "%s: device %d beyond the %d supported", name, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(LS_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", name, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LS_OK;
+}
+
 }  // namespace
 }  // namespace ls
 
@@ -954,6 +989,30 @@ int ls_layernorm_bwd_params(void* dgamma, void* dbeta, int64_t rows, int64_t hid
                   reinterpret_cast<const float*>(ws ? ws + kBwdHeaderBytes : nullptr), max_blocks, h32);
     set_dispatch(rows > 0 ? "layernorm_bwd_params/fixed_order" : "layernorm_bwd_params/zero_rows");
     return launch_status(name);
+}
+
+size_t ls_layernorm_bwd_noalloc_max_bytes(void) { return ls::kScratchBytes; }
+
+int ls_layernorm_bwd_noalloc(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
+                             const void* gamma, const float* mean, const float* rstd, int64_t rows,
+                             int64_t hidden, void* stream) {
+    using namespace ls;
+    const char* name = "ls_layernorm_bwd_noalloc";
+    if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
+    if (hidden > kMaxHidden)
+        return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
+    const size_t need = ls_layernorm_bwd_workspace_bytes(rows, hidden);
+    if (need > kScratchBytes)
+        return fail(LS_ERR_WORKSPACE,
+                    "%s: [%lld, %lld] needs %zu bytes of scratch, more than the %zu this entry point holds "
+                    "(use ls_layernorm_bwd with a workspace)",
+                    name, (long long)rows, (long long)hidden, need, kScratchBytes);
+    void* ws = nullptr;
+    if (rows > 0 && hidden > 0) {
+        if (const int rc = scratch_for_current_device(name, &ws)) return rc;
+    }
+    return ls_layernorm_bwd(dx, dgamma, dbeta, dy, x, gamma, mean, rstd, rows, hidden, ws, kScratchBytes,
+                            stream);
 }
 
 int ls_layernorm_bwd(void* dx, void* dgamma, void* dbeta, const void* dy, const void* x,
