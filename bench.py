@@ -406,10 +406,12 @@ def cpu_worker(s0, nseq, seconds):
 # shape, Adam over the 350M-parameter workspace)
 # ---------------------------------------------------------------------------
 
-def extra_rows(torch, ops):
+def extra_rows(torch, ops, eager=False):
     """The rows outside the C3 chain, each on rotated buffer sets (cold): the
     elementwise backward pair at the C3 shapes, the C4 embedding forward and
-    backward, and Adam over the 350M-parameter workspace."""
+    backward, and Adam over the 350M-parameter workspace.  eager: every call
+    a few times, untimed, outside graphs (the profiler's counter runs
+    attribute counters per dispatch)."""
     import numpy as np
 
     import synth
@@ -421,6 +423,11 @@ def extra_rows(torch, ops):
 
     def cold(calls, reps=10):
         """Mean time per call of one graph holding one call per rotated set."""
+        if eager:
+            for c in calls[:3]:
+                c()
+            torch.cuda.synchronize()
+            return float("nan")
         for c in calls:
             c()
         torch.cuda.synchronize()
@@ -607,7 +614,7 @@ def extra_rows(torch, ops):
                                 hp["weight_decay"], step[0], hp["grad_scale"], hp["decoupled_wd"])
     adam()
     torch.cuda.synchronize()
-    iters = 20
+    iters = 2 if eager else 20
     a, b = ev(), ev()
     a.record()
     for _ in range(iters):
@@ -632,11 +639,11 @@ def extra_rows(torch, ops):
     torch.cuda.synchronize()
     a, b = ev(), ev()
     a.record()
-    for i in range(5 * 8):
+    for i in range(0 if eager else 5 * 8):
         adam_range(i)
     b.record()
     torch.cuda.synchronize()
-    us_s = a.elapsed_time(b) / 40 * 1e3
+    us_s = float("nan") if eager else a.elapsed_time(b) / 40 * 1e3
     out["adam_workspace_shard"] = row(f"{n8 / 1e6:.2f}M params (350M sharded 8 ways by range), 1 launch", us_s,
                                       22 * n8, params_per_s=round(n8 / us_s * 1e6, 1))
 
@@ -650,7 +657,7 @@ def extra_rows(torch, ops):
     v.zero_()
     prev = prm.clone()
     unchanged = []
-    for st in range(1, synth.ADAM_STEPS + 1):
+    for st in range(1, 1 if eager else synth.ADAM_STEPS + 1):
         ops.adam_workspace_step(prm, grd, m, v, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
                                 hp["weight_decay"], st, hp["grad_scale"], hp["decoupled_wd"])
         unchanged.append(round((prm == prev).sum().item() / n, 7))
@@ -751,6 +758,175 @@ def write_chain_traffic(f_rows, w_rows, f_scale, w_scale, per_kernel):
         if seen:
             out.append(f"| **{op}** | all | | | | **{tot:.2f}** | {per[op] / 1e6:.2f} | **{tot * 1e6 / per[op]:.3f}** |")
     path = os.path.join(ROOT, "profiles", "chain_bert_base_4096tok_traffic.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("wrote", path)
+
+
+def other_rows_bytes():
+    """Algorithmic bytes per call of every row outside the chain, at the shapes
+    extra_rows runs them (the same formulas)."""
+    import numpy as np
+
+    import synth
+    T, H, F = synth.C3.tokens, synth.C3.hidden, synth.C3.ffn
+    H3 = 3 * H
+    T4, H4, V4, L4 = synth.C4.tokens, synth.C4.hidden, synth.C4.vocab, synth.C4.seq
+    distinct = int(np.unique(synth.embedding_inputs()["ids"]).size)
+    per4, _, _ = chain_bytes(T4, H4, synth.C4.ffn, synth.C4.heads, L4)
+    nb_, nk_ = 128, 4
+    n = synth.C5_PARAMS
+    out = {
+        "bias_dropout_residual_bwd [4096,768]": 4 * T * H + 2 * H,
+        "bias_relu_dropout_bwd [4096,3072]": 6 * T * F + 2 * F,
+        "bias_qkv_split [4096,2304]": 4 * T * H3 + 2 * H3,
+        "bias_qkv_split_bwd [4096,2304]": 4 * T * H3 + 2 * H3,
+        "embedding_fwd C4": 4 * T4 + 2 * H4 * distinct + 2 * H4 * L4 + 2 * T4 * H4,
+        "embedding_bwd C4": 4 * T4 + 2 * T4 * H4 + 8 * H4 * distinct,
+        "embedding_bwd zero fill C4": 4 * V4 * H4,
+        "cross_entropy_fwd C4": 2 * T4 * V4 + 4 * T4 + 8 * T4,
+        "cross_entropy_bwd C4": 4 * T4 * V4 + 4 * T4 + 4 * T4,
+        "beam_topk 128x4x32768": 4 * nb_ * nk_ * V4 + 4 * nb_ * nk_ + 8 * nb_ * nk_,
+        "adam_workspace_step 350M": 22 * n,
+        "adam_workspace_shard 43.75M": 22 * (n // 8),
+    }
+    for k in ("bias_dropout_residual", "bias_dropout_residual_layernorm", "bias_relu_dropout", "layernorm_fwd",
+              "layernorm_bwd", "softmax_fwd", "softmax_bwd"):
+        out[f"{k} C4"] = per4[k]
+    return out
+
+
+# Each row outside the chain: (row, kernel-name pattern, grid-size choice, follower).  "largest" /
+# "smallest" pick the dispatches of that pattern with the largest / smallest grid (the same kernel
+# at two shapes); a follower pattern (a column finalisation) is attributed to the row whose kernel
+# is the nearest library dispatch before it.
+ROW_KERNELS = (
+    ("bias_dropout_residual_bwd [4096,768]", r"ew_bwd_vec_kernelILb0E", None, "colsum_finalize_kernel"),
+    ("bias_relu_dropout_bwd [4096,3072]", r"ew_bwd_vec_kernelILb1E", None, "colsum_finalize_kernel"),
+    ("bias_dropout_residual C4", r"elementwise_vec_kernelILb1ELb0ELb1E", None, None),
+    ("bias_dropout_residual_layernorm C4", r"ln_fwd_kernel\w*Lb1EE", None, None),
+    ("bias_relu_dropout C4", r"elementwise_vec_kernelILb0ELb1ELb1E", "largest", None),
+    ("layernorm_fwd C4", r"ln_fwd_kernel\w*Lb0EE", None, None),
+    ("layernorm_bwd C4", r"ln_bwd_kernel", None, "ln_bwd_finalize_kernel"),
+    ("softmax_fwd C4", r"softmax_fwd_kernel", None, None),
+    ("softmax_bwd C4", r"softmax_bwd_kernel", None, None),
+    ("bias_qkv_split [4096,2304]", r"qkv_split_vec_kernel", None, None),
+    ("bias_qkv_split_bwd [4096,2304]", r"qkv_split_bwd_vec_kernel", None, "colsum_finalize_kernel"),
+    ("embedding_fwd C4", r"emb_fwd_vec_kernel", None, None),
+    ("embedding_bwd C4", r"emb_bwd_sorted_kernel", None, None),
+    ("embedding_bwd zero fill C4", r"fill_zero_kernel", None, None),
+    ("cross_entropy_fwd C4", r"xent_fwd_vec_kernel", None, None),
+    ("cross_entropy_bwd C4", r"xent_bwd_vec_kernel", None, None),
+    ("beam_topk 128x4x32768", r"beam_row_topk_kernel", None, "beam_merge_kernel"),
+    ("adam_workspace_step 350M", r"adam_kernel", "largest", None),
+    ("adam_workspace_shard 43.75M", r"adam_kernel", "smallest", None),
+)
+
+
+def summarize_rows(fetch_csv, write_csv):
+    """HBM bytes per call of every row outside the chain, from FETCH_SIZE and
+    WRITE_SIZE passes of `bench.py --rows-only --eager`, scaled like the
+    chain's counters (by torch's 1 GiB device copy in the same run), against
+    the algorithmic bytes; written to profiles/other_rows_traffic.md."""
+    import csv
+    copy_bytes = 1 << 30
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r.get("Counter_Name") == counter]
+        calib = max(float(r["Counter_Value"]) for r in rows if not r["Kernel_Name"].startswith("_ZN2ls"))
+        lib = sorted((r for r in rows if r["Kernel_Name"].startswith("_ZN2ls")), key=lambda r: int(r["Dispatch_Id"]))
+        return lib, copy_bytes / (calib * 1024)
+
+    f_rows, f_scale = load(fetch_csv, "FETCH_SIZE")
+    w_rows, w_scale = load(write_csv, "WRITE_SIZE")
+
+    def per_row(lib, scale):
+        """row -> (bytes per dispatch of its kernel, of its follower, dispatch counts)."""
+        owner_of = {}                   # dispatch index -> row, for the kernels of every row
+        res = {}
+        for row, pat, pick, follow in ROW_KERNELS:
+            hits = [i for i, r in enumerate(lib) if re.search(pat, r["Kernel_Name"])]
+            if pick and hits:
+                grids = [int(lib[i]["Grid_Size"]) for i in hits]
+                want = max(grids) if pick == "largest" else min(grids)
+                hits = [i for i, g in zip(hits, grids) if g == want]
+            for i in hits:
+                owner_of[i] = row
+            main = [float(lib[i]["Counter_Value"]) * 1024 * scale for i in hits]
+            res[row] = [main, [], follow]
+        for i, r in enumerate(lib):
+            for row, (main, fol, follow) in res.items():
+                if follow and re.search(follow, r["Kernel_Name"]):
+                    j = i - 1
+                    while j >= 0 and j not in owner_of:
+                        j -= 1
+                    if j >= 0 and owner_of[j] == row:
+                        fol.append(float(r["Counter_Value"]) * 1024 * scale)
+        return res
+
+    fr, wr = per_row(f_rows, f_scale), per_row(w_rows, w_scale)
+    alg = other_rows_bytes()
+    mean = lambda v: sum(v) / len(v) if v else 0.0  # noqa: E731
+    out = ["# HBM traffic per call: the rows outside the BERT-base chain", "",
+           "Two `rocprofv3 --pmc` passes of `bench.py --rows-only --eager` (FETCH_SIZE, then WRITE_SIZE, KiB per "
+           f"dispatch), scaled by what the same counters read for torch's 1 GiB device copy in the same runs (FETCH "
+           f"x{f_scale:.3f}, WRITE x{w_scale:.3f}). A row's bytes are its kernel's mean per dispatch plus, where it "
+           "has one, the mean of its second kernel (a column finalisation or merge). Commands, from the repository "
+           "root on the MI355X machine (R = repository root, OUT = an output folder):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE -d $OUT/rows_fetch -o fetch "
+           "--output-format csv -- python3 $R/bench.py --rows-only --eager",
+           "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE -d $OUT/rows_write -o write "
+           "--output-format csv -- python3 $R/bench.py --rows-only --eager",
+           "python bench.py --summarize-rows $OUT/rows_fetch/fetch_counter_collection.csv "
+           "$OUT/rows_write/write_counter_collection.csv", "```", "",
+           "| row | dispatches | read MB | written MB | measured MB | algorithmic MB | measured / algorithmic |",
+           "|---|---|---|---|---|---|---|"]
+    for row, _, _, _ in ROW_KERNELS:
+        fm, ff, _ = fr[row]
+        wm, wf, _ = wr[row]
+        if not fm or not wm:
+            out.append(f"| {row} | 0 | | | | {alg[row] / 1e6:.2f} | |")
+            continue
+        rd, wt = mean(fm) + mean(ff), mean(wm) + mean(wf)
+        n = f"{len(fm)}" + (f" + {len(ff)}" if ff else "")
+        out.append(f"| {row} | {n} | {rd / 1e6:.2f} | {wt / 1e6:.2f} | {(rd + wt) / 1e6:.2f} | {alg[row] / 1e6:.2f} | "
+                   f"{(rd + wt) / alg[row]:.3f} |")
+    path = os.path.join(ROOT, "profiles", "other_rows_traffic.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def summarize_trace(trace_csv, out_name, title, note, command):
+    """Per-kernel duration statistics of the library's kernels from a
+    rocprofv3 kernel trace (one row per kernel and grid size), written to
+    profiles/<out_name> with the command that made the trace."""
+    import csv
+    import statistics
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        if not name.startswith("_ZN2ls"):
+            continue
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((name, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))), []).append(d)
+    total = sum(sum(v) for v in groups.values())
+    rows = []
+    for (name, blocks), v in groups.items():
+        v = sorted(v)
+        q = lambda f: v[min(len(v) - 1, int(f * len(v)))]  # noqa: E731
+        short = name if len(name) <= 110 else name[:107] + "..."
+        rows.append((sum(v), f"| `{short}` | {blocks} | {len(v)} | {statistics.fmean(v):.2f} | {q(0.1):.2f} | "
+                             f"{statistics.median(v):.2f} | {q(0.9):.2f} | {v[0]:.2f} | {v[-1]:.2f} | "
+                             f"{100 * sum(v) / total:.1f} |"))
+    rows.sort(reverse=True)
+    out = [f"# rocprofv3 kernel statistics: {title}", "", note, "",
+           "Command (from the repository root on the MI355X machine; R = repository root, OUT = an output folder):",
+           "", "```", command, "```", "",
+           "Durations per dispatch from the kernel trace (microseconds); one row per kernel and grid size.", "",
+           "| kernel | blocks | calls | avg us | p10 us | median us | p90 us | min us | max us | % of library time |",
+           "|---|---|---|---|---|---|---|---|---|---|"] + [r for _, r in rows]
+    path = os.path.join(ROOT, "profiles", out_name)
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
     print("wrote", path)
@@ -904,6 +1080,9 @@ def main():
                     help="launch every kernel directly instead of replaying HIP graphs (profiler runs)")
     ap.add_argument("--no-info", action="store_true", help="skip the per-kernel and warm-chain information")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--rows-only", action="store_true",
+                    help="only the rows outside the chain (with --eager: untimed, for counter runs)")
+    ap.add_argument("--summarize-rows", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--cpu-worker", nargs=3, metavar=("SEQ0", "NSEQ", "SECONDS"), help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_worker:
@@ -911,6 +1090,9 @@ def main():
         return 0
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return 0
+    if args.summarize_rows:
+        summarize_rows(*args.summarize_rows)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the operators "
@@ -938,6 +1120,9 @@ def main():
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+    if args.rows_only:
+        print(json.dumps({"other_rows": extra_rows(torch, ops, eager=args.eager)}), flush=True)
+        return 0
 
     sets, per, counts, total = build_sets(torch, lib, shape, args.sets, p, seed, eps)
     footprint = sum(sum(t.numel() * t.element_size() for t in s.t.values()) for s in sets)
