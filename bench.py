@@ -673,6 +673,19 @@ def extra_rows(torch, ops, eager=False):
 # rocprofv3 counter summary -> profiles/
 # ---------------------------------------------------------------------------
 
+def is_library_kernel(name):
+    """Kernels of this library in a rocprofv3 table: templates appear mangled,
+    the others demangled."""
+    return name.startswith("_ZN2ls") or name.startswith("ls::")
+
+
+def calibration_kib(rows):
+    """The counter value of the 1 GiB calibration copy: the run's first device
+    copy (bench.py makes it before anything else)."""
+    copies = sorted((r for r in rows if "copyBuffer" in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+    return float(copies[0]["Counter_Value"]) if copies else None
+
+
 def summarize_counters(fetch_csv, write_csv):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel, scaled by
     what the same counters read for torch's 1 GiB device copy (a plain copy
@@ -692,9 +705,7 @@ def summarize_counters(fetch_csv, write_csv):
     f_dom, nf = per_kernel(f_rows, is_dom)
     w_dom, nw = per_kernel(w_rows, is_dom)
     copy_bytes = 1 << 30
-    # the calibration copy is the largest non-library dispatch
-    f_copy = max((float(r["Counter_Value"]) for r in f_rows if not r["Kernel_Name"].startswith("_ZN2ls")), default=None)
-    w_copy = max((float(r["Counter_Value"]) for r in w_rows if not r["Kernel_Name"].startswith("_ZN2ls")), default=None)
+    f_copy, w_copy = calibration_kib(f_rows), calibration_kib(w_rows)
     f_scale = copy_bytes / (f_copy * 1024) if f_copy else None
     w_scale = copy_bytes / (w_copy * 1024) if w_copy else None
     res = {
@@ -833,8 +844,8 @@ def summarize_rows(fetch_csv, write_csv):
 
     def load(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r.get("Counter_Name") == counter]
-        calib = max(float(r["Counter_Value"]) for r in rows if not r["Kernel_Name"].startswith("_ZN2ls"))
-        lib = sorted((r for r in rows if r["Kernel_Name"].startswith("_ZN2ls")), key=lambda r: int(r["Dispatch_Id"]))
+        calib = calibration_kib(rows)
+        lib = sorted((r for r in rows if is_library_kernel(r["Kernel_Name"])), key=lambda r: int(r["Dispatch_Id"]))
         return lib, copy_bytes / (calib * 1024)
 
     f_rows, f_scale = load(fetch_csv, "FETCH_SIZE")
@@ -906,10 +917,12 @@ def summarize_trace(trace_csv, out_name, title, note, command):
     groups = {}
     for r in csv.DictReader(open(trace_csv)):
         name = r["Kernel_Name"]
-        if not name.startswith("_ZN2ls"):
+        if not is_library_kernel(name):
             continue
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        groups.setdefault((name, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))), []).append(d)
+        grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+        wg = int(r["Workgroup_Size_X"]) * int(r.get("Workgroup_Size_Y") or 1) * int(r.get("Workgroup_Size_Z") or 1)
+        groups.setdefault((name, grid // max(1, wg)), []).append(d)
     total = sum(sum(v) for v in groups.values())
     rows = []
     for (name, blocks), v in groups.items():
@@ -1083,6 +1096,7 @@ def main():
     ap.add_argument("--rows-only", action="store_true",
                     help="only the rows outside the chain (with --eager: untimed, for counter runs)")
     ap.add_argument("--summarize-rows", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("chain|rows", "KERNEL_TRACE_CSV"))
     ap.add_argument("--cpu-worker", nargs=3, metavar=("SEQ0", "NSEQ", "SECONDS"), help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_worker:
@@ -1093,6 +1107,27 @@ def main():
         return 0
     if args.summarize_rows:
         summarize_rows(*args.summarize_rows)
+        return 0
+    if args.summarize_trace:
+        which, path = args.summarize_trace
+        if which == "chain":
+            summarize_trace(path, "chain_bert_base_4096tok_kernel_stats.md",
+                            "BERT-base layer non-GEMM step (4096 tokens, hidden 768, FFN 3072), 12 rotated buffer sets",
+                            "Under the kernel trace every dispatch waits for the profiler, so each kernel starts on an "
+                            "idle GPU and its end includes the profiler's completion handling: durations are longer "
+                            "than in the untraced step (compare p10 with the live figures in the bench line).",
+                            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/prof_trace -o trace "
+                            "--output-format csv -- python3 $R/bench.py --steps 200 --warmup 20 --no-cpu --no-extra "
+                            "--no-info\npython $R/bench.py --summarize-trace chain $OUT/prof_trace/trace_kernel_trace.csv")
+        else:
+            summarize_trace(path, "other_rows_kernel_stats.md", "rows outside the chain",
+                            "Elementwise backwards and bias + Q/K/V split at the BERT-base shapes; the chain's kernels "
+                            "at the Transformer-big shapes; embedding, cross-entropy (8192 tokens, vocabulary 32768) "
+                            "and HARS top-k (128 x 4 x 32768); Adam over 350M parameters and one 8-way shard of it. "
+                            "Each row on rotated buffer sets, as in bench.py's other_rows.",
+                            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/rows_trace -o rows "
+                            "--output-format csv -- python3 $R/bench.py --rows-only\npython $R/bench.py "
+                            "--summarize-trace rows $OUT/rows_trace/rows_kernel_trace.csv")
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the operators "
