@@ -454,7 +454,8 @@ def assert_fused_z(z, rz, tag):
 
 
 FUSED_SHAPES = [(128, 256), (4096, 768), (8192, 1024), (77, 96), (33, 512), (9, 1536), (3, 4096), (20, 13),
-                (1030, 767), (5, 2048), (300, 768), (1, 8), (16384, 256), (4, 4095)]
+                (1030, 767), (5, 2048), (300, 768), (1, 8), (16384, 256), (4, 4095), (45, 520), (33, 640),
+                (1, 768)]
 
 
 @pytest.mark.parametrize("rows,h", FUSED_SHAPES)
