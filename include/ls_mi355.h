@@ -220,8 +220,10 @@ int ls_layernorm_fwd(void* y, float* mean, float* rstd, const void* x, const voi
  *     z = residual + Dropout(x + bias)      (exactly ls_bias_dropout_residual)
  *     (y, mean, rstd) = LayerNorm(z)        (exactly ls_layernorm_fwd of z)
  * z is rounded to fp16 and stored (the LayerNorm backward reads it), and the
- * statistics are those of the stored z, so the outputs are bit-identical to
- * the two calls one after the other; z is not read back from memory.
+ * statistics are those of the stored z; z is not read back from memory.  z
+ * is bit-identical to ls_bias_dropout_residual's output; y, mean and rstd
+ * equal ls_layernorm_fwd's of that z up to the order of the fp32 sums (rows
+ * of 65-96 16-byte vectors take 32 lanes each here, 64 there).
  * x, residual, z, y: fp16 [rows, hidden]; bias, gamma, beta: fp16 [hidden];
  * mean, rstd: fp32 [rows].  Dropout as in ls_bias_dropout_residual (flat
  * element index row * hidden + col, site `offset`).  z may alias x or

@@ -482,11 +482,15 @@ def test_bias_dropout_residual_layernorm(ls, rows, h, p):
     sigma = 1.0 / rrstd.astype(np.float64)
     assert_fp32(host(mean), rmean, tag + " mean", floor=sigma)
     assert_fp32(host(rstd), rrstd, tag + " rstd")
+    # against the two standalone operators: z bit for bit; y and the
+    # statistics to rounding (the fused kernel may give a row to fewer lanes,
+    # so its fp32 sums run in another order)
     z2 = ls.bias_dropout_residual(dev(x), dev(b), dev(r), p, SEED, off)
     y2, mean2, rstd2 = ls.layernorm_fwd(z2, dev(gamma), dev(beta), eps)
     assert np.array_equal(host(z).view(np.uint16), host(z2).view(np.uint16)), tag + ": z differs from the separate op"
-    assert np.array_equal(host(y).view(np.uint16), host(y2).view(np.uint16)), tag + ": y differs from the separate ops"
-    assert np.array_equal(host(mean), host(mean2)) and np.array_equal(host(rstd), host(rstd2)), tag
+    assert_fp16(host(y), host(y2), tag + " y against the separate ops")
+    assert_fp32(host(mean), host(mean2), tag + " mean against the separate ops", floor=sigma)
+    assert_fp32(host(rstd), host(rstd2), tag + " rstd against the separate ops")
 
 
 def test_bias_dropout_residual_layernorm_aliasing_offsets_and_empty(ls):
