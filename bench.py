@@ -1264,7 +1264,7 @@ def main():
         us1 = kernels["bias_relu_dropout"]["us"]
         elems = shape.tokens * shape.ffn
         philox = {"kernel": f"bias_relu_dropout [{shape.tokens},{shape.ffn}]", "us_p0.1": us1, "us_p0": round(us0, 2),
-                  "extra_us": round(us1 - us0, 2), "extra_ns_per_element": round((us1 - us0) * 1e3 / elems, 6),
+                  "extra_us": round(us1 - us0, 2), "extra_ps_per_element": round((us1 - us0) * 1e6 / elems, 4),
                   "share_of_kernel": round((us1 - us0) / us1, 4),
                   # from the generated code: per call of 8 decisions, 20 v_mad_u64_u32 and 20 v_bitop3_b32
                   # (ten rounds, two products and two three-way XORs each), then 8 compares and selects
