@@ -151,7 +151,7 @@ class KernelEvents:
 class ChainSet:
     """Device buffers of one step, and its launches as (name, bytes, call)."""
 
-    def __init__(self, torch, inputs, shape, lib, per_bytes, p, seed, eps, fused=True):
+    def __init__(self, torch, inputs, shape, lib, per_bytes, p, seed, eps, fused=True, batched_params=True):
         d = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
         self.torch = torch
         self.t = {k: d(v) for k, v in inputs.items()}
@@ -181,6 +181,23 @@ class ChainSet:
         S = torch.cuda.current_stream().cuda_stream
         import synth
         pb = per_bytes
+        in2 = ("layernorm_bwd", pb["layernorm_bwd_input"], lib.ls_layernorm_bwd_input,
+               (P["dx2"], P["grad_y2"], P["ffn_out"], P["gamma2"], P["mean2"], P["rstd2"], T, H, P["ws2"], ws, S))
+        in1 = ("layernorm_bwd", pb["layernorm_bwd_input"], lib.ls_layernorm_bwd_input,
+               (P["dx1"], P["grad_y1"], P["attn_out"], P["gamma1"], P["mean1"], P["rstd1"], T, H, P["ws1"], ws, S))
+        if batched_params:
+            import ctypes
+            vp, i64, sz = ctypes.c_void_p * 2, ctypes.c_int64 * 2, ctypes.c_size_t * 2
+            # host arrays of the two jobs, kept alive with the set
+            self.jobs = (vp(P["dg2"], P["dg1"]), vp(P["db2"], P["db1"]), i64(T, T), i64(H, H),
+                         vp(P["ws2"], P["ws1"]), sz(ws, ws))
+            bwd = [in2, in1, ("layernorm_bwd_params", 2 * pb["layernorm_bwd_params"],
+                              lib.ls_layernorm_bwd_params_batched, (2, *self.jobs, S), "side")]
+        else:
+            bwd = [in2, ("layernorm_bwd_params", pb["layernorm_bwd_params"], lib.ls_layernorm_bwd_params,
+                         (P["dg2"], P["db2"], T, H, P["ws2"], ws, S), "side"),
+                   in1, ("layernorm_bwd_params", pb["layernorm_bwd_params"], lib.ls_layernorm_bwd_params,
+                         (P["dg1"], P["db1"], T, H, P["ws1"], ws, S), "side")]
         # (name, algorithmic bytes, ctypes function, args)
         if fused:
             sub1 = [("bias_dropout_residual_layernorm", pb["bias_dropout_residual_layernorm"],
@@ -210,15 +227,9 @@ class ChainSet:
             *sub2,
             # LayerNorm backward as its two calls: the input gradient, then the
             # parameter gradients (consumed only by the optimizer; tagged so a
-            # caller may put them on a side stream).
-            ("layernorm_bwd", pb["layernorm_bwd_input"], lib.ls_layernorm_bwd_input,
-             (P["dx2"], P["grad_y2"], P["ffn_out"], P["gamma2"], P["mean2"], P["rstd2"], T, H, P["ws2"], ws, S)),
-            ("layernorm_bwd_params", pb["layernorm_bwd_params"], lib.ls_layernorm_bwd_params,
-             (P["dg2"], P["db2"], T, H, P["ws2"], ws, S), "side"),
-            ("layernorm_bwd", pb["layernorm_bwd_input"], lib.ls_layernorm_bwd_input,
-             (P["dx1"], P["grad_y1"], P["attn_out"], P["gamma1"], P["mean1"], P["rstd1"], T, H, P["ws1"], ws, S)),
-            ("layernorm_bwd_params", pb["layernorm_bwd_params"], lib.ls_layernorm_bwd_params,
-             (P["dg1"], P["db1"], T, H, P["ws1"], ws, S), "side"),
+            # caller may put them on a side stream).  batched_params: both
+            # LayerNorms' parameter gradients in one call after both input calls.
+            *bwd,
             ("softmax_bwd", pb["softmax_bwd"], lib.ls_softmax_bwd,
              (P["dscores"], P["probs"], P["grad_probs"], B * NH * L, L, S)),
         ]
@@ -277,11 +288,11 @@ def replay_us(torch, graphs, reps):
     return e0.elapsed_time(e1) * 1e3 / (reps * len(graphs))
 
 
-def build_sets(torch, lib, shape, nsets, p, seed, eps, config=3, fused=True):
+def build_sets(torch, lib, shape, nsets, p, seed, eps, config=3, fused=True, batched_params=True):
     import synth
     per, counts, total = chain_bytes(shape.tokens, shape.hidden, shape.ffn, shape.heads, shape.seq, fused)
     inputs = synth.chain_inputs(shape, config=config)
-    sets = [ChainSet(torch, inputs, shape, lib, per, p, seed, eps, fused) for _ in range(nsets)]
+    sets = [ChainSet(torch, inputs, shape, lib, per, p, seed, eps, fused, batched_params) for _ in range(nsets)]
     return sets, per, counts, total
 
 
@@ -753,17 +764,21 @@ def write_chain_traffic(f_rows, w_rows, f_scale, w_scale, per_kernel):
            "-o write --output-format csv -- python3 $R/bench.py --eager --steps 12 --warmup 2 --no-cpu --no-extra --no-info",
            "python bench.py --summarize-counters $OUT/prof_fetch/fetch_counter_collection.csv "
            "$OUT/prof_write/write_counter_collection.csv", "```", "",
+           "Per dispatch for each kernel; per call for each operator (a kernel that one dispatch runs for "
+           "several calls, like the batched LayerNorm parameter-gradient finalisation, is counted in proportion "
+           "to its dispatches per call of the operator's first kernel).", "",
            "| operator | kernel | dispatches | read MB | written MB | measured MB | algorithmic MB | measured / algorithmic |",
            "|---|---|---|---|---|---|---|---|"]
     for op, syms in CHAIN_SYMBOLS:
-        tot, seen = 0.0, False
+        tot, seen, calls = 0.0, False, None
         for sym in syms:
             f, nf = per_kernel(f_rows, lambda k, s=sym: re.search(s, k) is not None)
             w, _ = per_kernel(w_rows, lambda k, s=sym: re.search(s, k) is not None)
             if f is None or w is None:
                 continue
             rd, wr = f * 1024 * f_scale / 1e6, w * 1024 * w_scale / 1e6
-            tot += rd + wr
+            calls = nf if calls is None else calls
+            tot += (rd + wr) * nf / calls
             seen = True
             out.append(f"| {op} | `{sym}` | {nf} | {rd:.2f} | {wr:.2f} | {rd + wr:.2f} | | |")
         if seen:
@@ -1045,21 +1060,25 @@ def attainable(torch, lib, check, cap_stream, dom_bytes):
 
 
 def step_variants(torch, lib, check, cap_stream, p, seed, eps, nsets=12, reps=20):
-    """The same BERT-base step in two other forms, each on its own rotated
-    sets: bias+dropout+residual and LayerNorm as two operators each
-    (unfused), and the fused step with the LayerNorm parameter gradients on a
-    side stream (a branch of the graph, joined at the end of the step)."""
+    """The same BERT-base step in other forms, each on its own rotated sets:
+    bias+dropout+residual and LayerNorm as two operators each and each
+    LayerNorm's parameter gradients in a call of their own (unfused); the
+    fused step with each LayerNorm's parameter gradients in a call of their
+    own; and the fused step with the batched parameter gradients on a side
+    stream (a branch of the graph, joined at the end of the step)."""
     import synth
     shape = synth.C3
     out = {}
     side = torch.cuda.Stream()         # default priority, like every stream here
-    for fused, side_ in ((False, None), (True, side)):
-        sets, per, counts, total = build_sets(torch, lib, shape, nsets, p, seed, eps, fused=fused)
+    for key, fused, batched, side_ in (("unfused", False, False, None),
+                                       ("fused_parameter_gradients_per_layernorm", True, False, None),
+                                       ("fused_parameter_gradients_on_side_stream", True, True, side)):
+        sets, per, counts, total = build_sets(torch, lib, shape, nsets, p, seed, eps, fused=fused,
+                                              batched_params=batched)
         for s in sets:
             s.run(check, side_)
         graphs = [capture_items(torch, s.launches, cap_stream, check, side_) for s in sets]
         us = replay_us(torch, graphs, reps)
-        key = "unfused" if not fused else "fused_parameter_gradients_on_side_stream"
         out[key] = {"calls_per_step": len(sets[0].launches), "us_per_step": round(us, 2), "bytes_per_step": total,
                     "GB/s": round(total / us / 1e3, 1), "tokens_per_s": round(shape.tokens / (us * 1e-6), 1)}
         del graphs, sets
@@ -1163,7 +1182,7 @@ def main():
     footprint = sum(sum(t.numel() * t.element_size() for t in s.t.values()) for s in sets)
     # The step runs on one stream: the LayerNorm parameter gradients in line.
     # (A side-stream branch for them, joined at the end of the step, measured
-    # 94 against 62 us per step: see step_variants.)
+    # far slower: see step_variants.)
     side = None
     for s in sets:                     # first launches outside any capture
         s.run(check, side)
@@ -1318,7 +1337,7 @@ def main():
                    "seq_len": shape.seq, "hidden": shape.hidden, "heads": shape.heads, "ffn": shape.ffn,
                    "dropout_p": p, "chain_bytes_per_step": total, "rotated_sets": args.sets,
                    "footprint_bytes": footprint, "launches_per_step": n_launch,
-                   "kernels_per_step": n_launch + counts["layernorm_bwd"],
+                   "kernels_per_step": n_launch,
                    "fused_bias_dropout_residual_layernorm": True},
         "roofline": {"bound": "hbm", "kernel": f"{DOMINANT} row kernel {DOMINANT_SHAPE}",
                      "achieved": round(achieved, 1),

@@ -303,6 +303,24 @@ int ls_layernorm_bwd_input(void* dx, const void* dy, const void* x, const void* 
 int ls_layernorm_bwd_params(void* dgamma, void* dbeta, int64_t rows, int64_t hidden, const void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Parameter-gradient finalisation of several LayerNorms in one launch: job i
+ * is exactly ls_layernorm_bwd_params(dgamma[i], dbeta[i], rows[i], hidden[i],
+ * workspace[i], workspace_bytes[i]).  A layer's (or a model's) LayerNorm
+ * gradients dgamma / dbeta are read only by the optimizer ([LS2] §2.3: the
+ * trainer updates the whole gradient workspace at once), so their
+ * finalisations can wait and share one launch; each job's workspace must
+ * hold its own input call's partials, complete and not overwritten.
+ * The arrays are host arrays of `count` entries; up to 16 jobs share a
+ * launch (more take several).  Jobs with hidden == 0 are skipped; rows == 0
+ * writes zeros without reading that job's workspace.  Every job is checked
+ * before anything is launched; the first failing job's error is returned
+ * (the message names the job) and nothing runs.  count == 0 launches nothing.
+ * Errors: LS_ERR_PARAM (count < 0, misaligned workspace), LS_ERR_NULL (a null
+ * array or pointer), and each job's errors as ls_layernorm_bwd_params. */
+int ls_layernorm_bwd_params_batched(int count, void* const* dgamma, void* const* dbeta, const int64_t* rows,
+                                    const int64_t* hidden, void* const* workspace, const size_t* workspace_bytes,
+                                    void* stream);
+
 /* Masked row softmax forward ([L10] slides 23-26) over attention scores
  * x, y: fp16 [batch, heads, q_len, k_len].  For row (b, h, i) the valid keys
  * are j < key_lengths[b] (clamped to [0, k_len]; all keys if key_lengths is

@@ -55,6 +55,8 @@ SIGNATURES = {
     "ls_layernorm_bwd_input": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64,
                                        c_void_p, c_size, c_void_p]),
     "ls_layernorm_bwd_params": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_size, c_void_p]),
+    "ls_layernorm_bwd_params_batched": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                c_void_p]),
     "ls_softmax_fwd": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p, c_int,
                                c_void_p]),
     "ls_softmax_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p]),

@@ -612,17 +612,34 @@ constexpr int kFinCols = 32;
 constexpr int kFinSlices = 16;
 constexpr unsigned kMaxBwdBlocks = kFinSlices * 16;
 
-// The partial-row count comes from the workspace header the row kernel
-// wrote, clamped to max_blocks (the count the workspace is sized for), so a
-// stale header cannot send a read past the partial rows; max_blocks == 0
-// (no rows) writes zeros without reading the workspace.
-__global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
-    half_t* dgamma, half_t* dbeta, const uint32_t* header, const float* partial, uint32_t max_blocks,
-    uint32_t h) {
+// Finalisations of up to kFinMaxJobs LayerNorms in one launch (a layer's or
+// a model's LayerNorms, whose parameter gradients wait for the optimizer):
+// job j takes blocks [first_block[j], first_block[j + 1]).  Each job's
+// partial-row count comes from the workspace header its row kernel wrote,
+// clamped to max_blocks (the count the workspace is sized for), so a stale
+// header cannot send a read past the partial rows; max_blocks == 0 (no rows)
+// writes zeros without reading the workspace.
+constexpr int kFinMaxJobs = 16;
+struct FinJobs {
+    uint32_t count;
+    uint32_t first_block[kFinMaxJobs + 1];
+    uint32_t h[kFinMaxJobs];
+    uint32_t max_blocks[kFinMaxJobs];
+    half_t* dgamma[kFinMaxJobs];
+    half_t* dbeta[kFinMaxJobs];
+    const uint32_t* header[kFinMaxJobs];
+    const float* partial[kFinMaxJobs];
+};
+
+__global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(const FinJobs jobs) {
     __shared__ float sums[kFinSlices][kFinCols];
-    const uint32_t nblocks = max_blocks ? min(header[0], max_blocks) : 0u;
+    uint32_t j = 0;                              // uniform over the block
+    while (j + 1 < jobs.count && blockIdx.x >= jobs.first_block[j + 1]) ++j;
+    const uint32_t h = jobs.h[j], max_blocks = jobs.max_blocks[j];
+    const float* partial = jobs.partial[j];
+    const uint32_t nblocks = max_blocks ? min(jobs.header[j][0], max_blocks) : 0u;
     const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
-    const uint32_t c = blockIdx.x * kFinCols + cl;
+    const uint32_t c = (blockIdx.x - jobs.first_block[j]) * kFinCols + cl;
     const uint32_t w = 2 * h;
     float v[16];
 #pragma unroll
@@ -639,8 +656,8 @@ __global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
         float t = 0.0f;
 #pragma unroll
         for (int s = 0; s < kFinSlices; ++s) t += sums[s][cl];
-        if (c < h) dgamma[c] = to_half(t);
-        else dbeta[c - h] = to_half(t);
+        if (c < h) jobs.dgamma[j][c] = to_half(t);
+        else jobs.dbeta[j][c - h] = to_half(t);
     }
 }
 
@@ -812,6 +829,67 @@ int scratch_for_current_device(const char* name, void** out) {
     return LS_OK;
 }
 
+// Checks one parameter-gradient finalisation (the arguments of
+// ls_layernorm_bwd_params); `who` names the call, and the job, in messages.
+int check_params_job(const char* who, const void* dgamma, const void* dbeta, int64_t rows, int64_t hidden,
+                     const void* workspace, size_t workspace_bytes) {
+    if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", who);
+    if (hidden == 0) return LS_OK;                 // nothing to write
+    if (hidden > kMaxHidden)
+        return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", who, (long long)hidden, (long long)kMaxHidden);
+    if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", who);
+    if (!dgamma || !dbeta) return fail(LS_ERR_NULL, "%s: null pointer", who);
+    if (rows > 0) {
+        if (!workspace) return fail(LS_ERR_NULL, "%s: null workspace", who);
+        const size_t need = ls_layernorm_bwd_workspace_bytes(rows, hidden);
+        if (workspace_bytes < need)
+            return fail(LS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, need);
+        if (!aligned16(workspace)) return fail(LS_ERR_PARAM, "%s: workspace must be 16-byte aligned", who);
+    }
+    return LS_OK;
+}
+
+// Launches the finalisation of checked jobs, kFinMaxJobs per launch (jobs
+// with hidden == 0 have nothing to write and are skipped), records the
+// dispatch and returns the number of launches.
+int launch_params_jobs(int count, void* const* dgamma, void* const* dbeta, const int64_t* rows,
+                        const int64_t* hidden, void* const* workspace, hipStream_t st) {
+    clear_hip_error();
+    int launches = 0, jobs_run = 0;
+    FinJobs fj{};
+    auto flush = [&]() {
+        if (fj.count == 0) return;
+        launch_kernel(ln_bwd_finalize_kernel, dim3(fj.first_block[fj.count]), dim3(kFinCols * kFinSlices), 0, st,
+                      fj);
+        ++launches;
+        fj = FinJobs{};
+    };
+    for (int i = 0; i < count; ++i) {
+        if (hidden[i] == 0) continue;
+        const uint32_t k = fj.count;
+        const auto* ws = static_cast<const char*>(workspace[i]);
+        const bool has_rows = rows[i] > 0;
+        fj.h[k] = static_cast<uint32_t>(hidden[i]);
+        fj.max_blocks[k] = has_rows ? bwd_max_blocks(rows[i]) : 0u;
+        fj.dgamma[k] = static_cast<half_t*>(dgamma[i]);
+        fj.dbeta[k] = static_cast<half_t*>(dbeta[i]);
+        // A job with no rows reads nothing: the kernel never dereferences these.
+        fj.header[k] = has_rows ? reinterpret_cast<const uint32_t*>(ws) : nullptr;
+        fj.partial[k] = has_rows ? reinterpret_cast<const float*>(ws + kBwdHeaderBytes) : nullptr;
+        fj.first_block[k + 1] =
+            fj.first_block[k] + static_cast<uint32_t>((2 * hidden[i] + kFinCols - 1) / kFinCols);
+        fj.count = k + 1;
+        ++jobs_run;
+        if (fj.count == kFinMaxJobs) flush();
+    }
+    flush();
+    char buf[96];
+    if (jobs_run == 0) snprintf(buf, sizeof(buf), "empty");
+    else snprintf(buf, sizeof(buf), "layernorm_bwd_params/fixed_order_jobs%d_launches%d", jobs_run, launches);
+    set_dispatch(buf);
+    return launches;
+}
+
 }  // namespace
 }  // namespace ls
 
@@ -967,38 +1045,38 @@ int ls_layernorm_bwd_input(void* dx, const void* dy, const void* x, const void* 
     return launch_status(name);
 }
 
+int ls_layernorm_bwd_params_batched(int count, void* const* dgamma, void* const* dbeta, const int64_t* rows,
+                                    const int64_t* hidden, void* const* workspace, const size_t* workspace_bytes,
+                                    void* stream) {
+    using namespace ls;
+    const char* name = "ls_layernorm_bwd_params_batched";
+    if (count < 0) return fail(LS_ERR_PARAM, "%s: negative count", name);
+    if (count > 0 && (!dgamma || !dbeta || !rows || !hidden || !workspace || !workspace_bytes))
+        return fail(LS_ERR_NULL, "%s: null array", name);
+    // Every job is checked before anything is launched.
+    for (int i = 0; i < count; ++i) {
+        char who[80];
+        snprintf(who, sizeof(who), "%s: job %d", name, i);
+        if (const int rc = check_params_job(who, dgamma[i], dbeta[i], rows[i], hidden[i], workspace[i],
+                                            workspace_bytes[i]))
+            return rc;
+    }
+    if (launch_params_jobs(count, dgamma, dbeta, rows, hidden, workspace, static_cast<hipStream_t>(stream)) == 0)
+        return LS_OK;
+    return launch_status(name);
+}
+
 int ls_layernorm_bwd_params(void* dgamma, void* dbeta, int64_t rows, int64_t hidden, const void* workspace,
                             size_t workspace_bytes, void* stream) {
     using namespace ls;
     const char* name = "ls_layernorm_bwd_params";
-    if (rows < 0 || hidden < 0) return fail(LS_ERR_SHAPE, "%s: negative shape", name);
-    if (hidden == 0) {
-        set_dispatch("empty");
+    if (const int rc = check_params_job(name, dgamma, dbeta, rows, hidden, workspace, workspace_bytes)) return rc;
+    void* ws = const_cast<void*>(workspace);
+    if (launch_params_jobs(1, &dgamma, &dbeta, &rows, &hidden, &ws, static_cast<hipStream_t>(stream)) == 0)
         return LS_OK;
-    }
-    if (hidden > kMaxHidden)
-        return fail(LS_ERR_UNSUPPORTED, "%s: hidden %lld > %lld", name, (long long)hidden, (long long)kMaxHidden);
-    if (rows >= (1ll << 31)) return fail(LS_ERR_SHAPE, "%s: rows must be < 2^31", name);
-    if (!dgamma || !dbeta) return fail(LS_ERR_NULL, "%s: null pointer", name);
-    unsigned max_blocks = 0;
-    if (rows > 0) {
-        if (!workspace) return fail(LS_ERR_NULL, "%s: null workspace", name);
-        const size_t need = ls_layernorm_bwd_workspace_bytes(rows, hidden);
-        if (workspace_bytes < need)
-            return fail(LS_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", name, workspace_bytes, need);
-        if (!aligned16(workspace)) return fail(LS_ERR_PARAM, "%s: workspace must be 16-byte aligned", name);
-        max_blocks = bwd_max_blocks(rows);
-    }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint32_t h32 = static_cast<uint32_t>(hidden);
-    const auto* ws = static_cast<const char*>(workspace);
-    clear_hip_error();
-    const unsigned fgrid = static_cast<unsigned>((2 * hidden + kFinCols - 1) / kFinCols);
-    launch_kernel(ln_bwd_finalize_kernel, dim3(fgrid), dim3(kFinCols * kFinSlices), 0, st,
-                  static_cast<half_t*>(dgamma), static_cast<half_t*>(dbeta), reinterpret_cast<const uint32_t*>(ws),
-                  reinterpret_cast<const float*>(ws ? ws + kBwdHeaderBytes : nullptr), max_blocks, h32);
+    const int rc = launch_status(name);
     set_dispatch(rows > 0 ? "layernorm_bwd_params/fixed_order" : "layernorm_bwd_params/zero_rows");
-    return launch_status(name);
+    return rc;
 }
 
 size_t ls_layernorm_bwd_noalloc_max_bytes(void) { return ls::kScratchBytes; }

@@ -6,6 +6,8 @@ library, and raises LsError on a non-zero status.  All arithmetic runs in the
 library's HIP kernels; nothing here computes on the host.
 """
 
+import ctypes
+
 import torch
 
 from ._lib import check, load
@@ -285,6 +287,31 @@ def layernorm_bwd_params(rows, hidden, workspace, dgamma=None, dbeta=None, devic
     check("ls_layernorm_bwd_params", load().ls_layernorm_bwd_params(
         _ptr(dgamma), _ptr(dbeta), int(rows), int(hidden), _ptr(workspace), nbytes, _stream()))
     return dgamma, dbeta
+
+
+def layernorm_bwd_params_batched(jobs, device="cuda"):
+    """layernorm_bwd_params for several LayerNorms in one launch.  jobs: a
+    list of (rows, hidden, workspace, dgamma, dbeta), dgamma / dbeta None to
+    allocate.  Returns [(dgamma, dbeta), ...] in job order."""
+    n = len(jobs)
+    outs = []
+    for rows, hidden, ws, dg, db in jobs:
+        _dev(ws, dg, db)
+        dg = torch.empty(hidden, dtype=_F16, device=device) if dg is None else dg
+        db = torch.empty(hidden, dtype=_F16, device=device) if db is None else db
+        outs.append((dg, db, ws))
+    ptrs = ctypes.c_void_p * max(n, 1)
+    i64s = ctypes.c_int64 * max(n, 1)
+    sizes = ctypes.c_size_t * max(n, 1)
+    dgs = ptrs(*[_ptr(o[0]) for o in outs])
+    dbs = ptrs(*[_ptr(o[1]) for o in outs])
+    wss = ptrs(*[_ptr(o[2]) for o in outs])
+    rows = i64s(*[int(j[0]) for j in jobs])
+    hid = i64s(*[int(j[1]) for j in jobs])
+    nb = sizes(*[0 if o[2] is None else o[2].numel() * o[2].element_size() for o in outs])
+    check("ls_layernorm_bwd_params_batched", load().ls_layernorm_bwd_params_batched(
+        n, dgs, dbs, rows, hid, wss, nb, _stream()))
+    return [(o[0], o[1]) for o in outs]
 
 
 def softmax_fwd(x, key_lengths=None, causal=False, y=None):

@@ -108,6 +108,37 @@ def test_layernorm_validation(lib):
     assert lib.ls_layernorm_bwd(None, None, FAKE, None, None, None, None, None, 0, 768, None, 0, s) == LS_ERR_NULL
 
 
+def test_layernorm_params_batched_validation(lib):
+    """The batched finalisation checks every job before launching anything;
+    the error names the first failing job."""
+    s = None
+    need = lib.ls_layernorm_bwd_workspace_bytes(4096, 768)
+    P = ctypes.c_void_p * 3
+    I = ctypes.c_int64 * 3
+    Z = ctypes.c_size_t * 3
+
+    def call(n, dg, db, rows, hid, ws, nb):
+        return lib.ls_layernorm_bwd_params_batched(n, P(*dg), P(*db), I(*rows), I(*hid), P(*ws), Z(*nb), s)
+
+    ok = ([FAKE] * 3, [FAKE] * 3, [4096, 0, 5], [768, 768, 0], [FAKE, None, None], [need, 0, 0])
+    assert lib.ls_layernorm_bwd_params_batched(-1, None, None, None, None, None, None, s) == LS_ERR_PARAM
+    assert lib.ls_layernorm_bwd_params_batched(0, None, None, None, None, None, None, s) == LS_OK
+    assert lib.ls_last_dispatch() == b"empty"
+    assert lib.ls_layernorm_bwd_params_batched(1, None, None, None, None, None, None, s) == LS_ERR_NULL
+    # job 2: hidden 0 is skipped (nothing to write, its pointers unread); only
+    # hidden == 0 jobs: nothing launched
+    assert call(3, [None] * 3, [None] * 3, [7, 0, 1], [0, 0, 0], [None] * 3, [0] * 3) == LS_OK
+    assert lib.ls_last_dispatch() == b"empty"
+    for job, field, bad, code in [(0, 5, need - 1, LS_ERR_WORKSPACE), (0, 4, None, LS_ERR_NULL),
+                                  (1, 0, None, LS_ERR_NULL), (0, 3, 5000, LS_ERR_UNSUPPORTED),
+                                  (1, 2, -1, LS_ERR_SHAPE), (0, 4, ctypes.c_void_p(0x1008), LS_ERR_PARAM),
+                                  (0, 2, 1 << 31, LS_ERR_SHAPE)]:
+        args = [list(a) for a in ok]
+        args[field][job] = bad
+        assert call(3, *args) == code, (job, field, bad)
+        assert f"ls_layernorm_bwd_params_batched: job {job}:".encode() in lib.ls_last_error()
+
+
 def test_softmax_validation(lib):
     s = None
     assert lib.ls_softmax_fwd(FAKE, FAKE, 2, 2, 4, -1, None, 0, s) == LS_ERR_SHAPE

@@ -558,6 +558,48 @@ def test_layernorm_bwd_split_calls(ls, rows, h, offset):
         assert np.array_equal(host(a).view(np.uint16), b.view(np.uint16)), f"{tag}: {what}"
 
 
+def test_layernorm_bwd_params_batched(ls):
+    """ls_layernorm_bwd_params_batched over 20 LayerNorms of mixed shapes
+    (more than one launch's 16 jobs; a job with no rows, one with no
+    columns): every job's dgamma / dbeta equal its own parameter call's bit
+    for bit, and the oracle's to the fp16 bar."""
+    shapes = [(4096, 768), (300, 768), (77, 96), (5, 2048), (1030, 767), (0, 768), (8192, 1024), (1, 8),
+              (64, 0), (129, 520)]
+    shapes = shapes + shapes[::-1]
+    jobs, refs = [], []
+    for i, (rows, h) in enumerate(shapes):
+        if h == 0:
+            jobs.append((rows, 0, None, None, None))
+            refs.append(None)
+            continue
+        dg = torch.full((h,), 7.0, dtype=torch.float16, device="cuda")
+        db = torch.full((h,), -7.0, dtype=torch.float16, device="cuda")
+        if rows == 0:
+            jobs.append((0, h, None, dg, db))
+            refs.append((np.zeros(h, np.float16), np.zeros(h, np.float16), None, None))
+            continue
+        x, gamma, beta, dy = ln_inputs(rows, h, 300 + i)
+        _, mean, rstd = oracle.layernorm_fwd(x, gamma, beta, synth.LN_EPS)
+        args = (dev(dy), dev(x), dev(gamma), dev(mean), dev(rstd))
+        ws = torch.empty(ls.layernorm_bwd_workspace_bytes(rows, h), dtype=torch.uint8, device="cuda")
+        ls.layernorm_bwd_input(*args, ws)
+        one = [host(t).copy() for t in ls.layernorm_bwd_params(rows, h, ws)]
+        _, rdg, rdb = oracle.layernorm_bwd(dy, x, gamma, mean, rstd)
+        jobs.append((rows, h, ws, dg, db))
+        refs.append((one[0], one[1], rdg, rdb))
+    out = ls.layernorm_bwd_params_batched(jobs)
+    assert last_dispatch() == "layernorm_bwd_params/fixed_order_jobs18_launches2", last_dispatch()
+    for (rows, h), (dg, db), ref in zip(shapes, out, refs):
+        if ref is None:
+            continue
+        tag = f"batched params {rows}x{h}"
+        assert np.array_equal(host(dg).view(np.uint16), ref[0].view(np.uint16)), tag + " dgamma"
+        assert np.array_equal(host(db).view(np.uint16), ref[1].view(np.uint16)), tag + " dbeta"
+        if ref[2] is not None:
+            assert_fp16(host(dg), ref[2], tag + " dgamma vs oracle")
+            assert_fp16(host(db), ref[3], tag + " dbeta vs oracle")
+
+
 def test_layernorm_bwd_zero_rows_and_stale_header(ls):
     """No rows: dgamma and dbeta are the sums over no rows, zeros, from the
     combined call and from the parameter call alone (no workspace).  A
