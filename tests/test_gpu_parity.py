@@ -270,7 +270,11 @@ def assert_xent_rows(loss, lse, dx, x, y, eps, ignore, g, what):
 
 def test_cross_entropy_c4_sampled_rows(ls):
     """Transformer-big criterion: logits [8192, 32768], Zipf targets, eps 0.1;
-    every row computed on the GPU, the oracle on 64 sampled rows."""
+    every row computed on the GPU, the oracle on 1024 sampled rows, and on
+    every row what holds at any size: max(x) <= lse <= max(x) + log V,
+    loss >= 0 (lse bounds both the target logit and the mean logit), and
+    the gradient row sums to zero (the softmax, the one-hot and the smoothing
+    floor each sum to one) within its fp16 rounding."""
     T, V = synth.C4.tokens, synth.C4.vocab
     x = synth.criterion_logits(0, T)
     y = synth.criterion_targets()
@@ -280,9 +284,23 @@ def test_cross_entropy_c4_sampled_rows(ls):
     gs = synth.CRITERION_LOSS_SCALE / T           # mean over tokens, times the loss scale
     dx = ls.cross_entropy_bwd(xd, yd, lse, synth.CRITERION_SMOOTHING, -1, gs)
     assert last_dispatch() == "cross_entropy_bwd/vec8"
-    rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(7).integers(0, T, 61)]))
-    assert_xent_rows(host(loss)[rows], host(lse)[rows], host(dx)[rows], x[rows], y[rows],
+    rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(7).integers(0, T, 1021)]))
+    hl, hs, hd = host(loss), host(lse), host(dx)
+    assert_xent_rows(hl[rows], hs[rows], hd[rows], x[rows], y[rows],
                      synth.CRITERION_SMOOTHING, -1, gs, "cross_entropy C4")
+    xmax = x.max(axis=1).astype(np.float64)
+    lse64 = hs.astype(np.float64)
+    assert np.all(lse64 >= xmax - 1e-6 * np.abs(xmax)), "lse below the row maximum"
+    assert np.all(lse64 <= xmax + np.log(V) + 1e-5 * np.abs(xmax) + 1e-5), "lse above max + log V"
+    assert np.all(hl.astype(np.float64) >= -1e-5 * np.maximum(np.abs(lse64), 1.0)), "negative loss"
+    d64 = hd.astype(np.float64)
+    rowsum = d64.sum(axis=1)
+    # each element within half an fp16 spacing of its fp32 value, the fp32
+    # values within a few ulps of exact: twice the spacings bounds the sum
+    spacing = np.spacing(np.abs(hd)).astype(np.float64)
+    bound = 2.0 * spacing.sum(axis=1) + 1e-6 * gs
+    bad = np.abs(rowsum) > bound
+    assert not bad.any(), f"gradient rows not summing to zero: {np.flatnonzero(bad)[:5]} {rowsum[bad][:5]}"
 
 
 @pytest.mark.parametrize("rows,v", [(37, 1001), (5, 8), (1, 1), (3, 50257), (64, 4096), (17, 16392), (9, 2048)])
@@ -865,20 +883,29 @@ def fp16_ulp(x):
     return 2.0 ** (e - 10)
 
 
-def assert_adam_update(p_gpu, p_ref, p0, tag, ulps=2):
+def assert_adam_update(p_gpu, p_ref, p0, tag, ulps=2, rare_ulps=10, rare_frac=1e-5):
     """The update itself, p - p0, against the oracle's: within `ulps` fp16
     spacings of the parameter (each step rounds p to fp16; fp32 and float64
-    arithmetic may round a step differently now and then).  A step that is
-    missing, halved, doubled or of the wrong sign moves p by many spacings
+    arithmetic may round a step differently now and then).  A parameter whose
+    step lies next to a rounding midpoint, where the fp32 result rounded to
+    fp16 (two roundings) and the float64 one fall on different sides, can do
+    so at every step (the workload's gradient is the same at every step), so
+    at most `rare_frac` of the parameters may differ by up to `rare_ulps`
+    spacings (each result stays within half a spacing per step of the exact
+    path: ten steps, ten spacings apart at most).  A step that is missing,
+    halved, doubled or of the wrong sign moves every p by many spacings
     (lr = 1e-4 is ~6 spacings at |p| = 0.02 per step) and fails."""
     d_gpu = np.asarray(p_gpu, np.float64) - np.asarray(p0, np.float64)
     d_ref = np.asarray(p_ref, np.float64) - np.asarray(p0, np.float64)
-    tol = ulps * fp16_ulp(np.maximum(np.abs(np.asarray(p_ref, np.float64)), np.abs(np.asarray(p0, np.float64))))
-    bad = ~(np.abs(d_gpu - d_ref) <= tol)
-    if bad.any():
-        i = int(np.argwhere(bad)[0][0])
+    sp = fp16_ulp(np.maximum(np.abs(np.asarray(p_ref, np.float64)), np.abs(np.asarray(p0, np.float64))))
+    diff = np.abs(d_gpu - d_ref)
+    bad = ~(diff <= ulps * sp)
+    worst = ~(diff <= rare_ulps * sp)
+    if worst.any() or bad.sum() > rare_frac * bad.size:
+        i = int(np.argwhere(worst if worst.any() else bad)[0][0])
         raise AssertionError(f"{tag}: update of {int(bad.sum())}/{bad.size} parameters off by more than {ulps} "
-                             f"fp16 spacings; first at {i}: {d_gpu[i]} vs oracle {d_ref[i]} (p0 {p0[i]})")
+                             f"fp16 spacings ({int(worst.sum())} by more than {rare_ulps}); first at {i}: "
+                             f"{d_gpu[i]} vs oracle {d_ref[i]} (p0 {p0[i]})")
     moved = np.count_nonzero(d_ref)
     assert moved == 0 or np.count_nonzero(d_gpu) >= 0.9 * moved, f"{tag}: parameters left unchanged"
 
@@ -944,8 +971,14 @@ def test_adam_large_steps(ls, decoupled):
 
 def test_adam_full_workspace_sampled(ls):
     """The 350M-parameter workspace of the Adam workload, ten single-launch
-    steps on the GPU; the oracle (element-wise) on 200k sampled parameters,
-    chunk boundaries and the last element included."""
+    steps on the GPU; the oracle (element-wise) on 4M sampled parameters,
+    chunk boundaries and the last element included.  Every parameter is also
+    held to what the workload's constant gradient fixes in closed form: with
+    zero-initialised moments and the same g' = g / grad_scale at every step,
+    m_t = (1 - beta1^t) g' and v_t = (1 - beta2^t) g'^2 (so the
+    bias-corrected step is lr * (g' / (|g'| + eps) + wd * p) each time), and
+    after ten steps p is within five fp16 spacings (half a spacing per step,
+    along a monotone path) of p0 - 10 lr (g' / (|g'| + eps) + wd p0)."""
     n = synth.C5_PARAMS
     nchunks = -(-n // synth.C5_CHUNK)
     p = np.empty(n, np.float16)
@@ -957,7 +990,7 @@ def test_adam_full_workspace_sampled(ls):
     hp = synth.ADAM_HYPER
     pt, gt = dev(p), dev(gr)
     mt, vt = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
-    idx = np.unique(np.concatenate([np.random.default_rng(5).integers(0, n, 200_000),
+    idx = np.unique(np.concatenate([np.random.default_rng(5).integers(0, n, 4_000_000),
                                     np.arange(0, n, synth.C5_CHUNK), [n - 1, n - 8, 7, 8]]))
     rp, rg = p[idx], gr[idx]
     rm, rv = np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
@@ -972,6 +1005,24 @@ def test_adam_full_workspace_sampled(ls):
     assert_adam_update(host(pt[ti]), rp, p[idx], tag)
     assert_fp32(host(mt[ti]), rm, tag + " exp_avg")
     assert_fp32(host(vt[ti]), rv, tag + " exp_avg_sq")
+    assert hp["decoupled_wd"], "the closed form below assumes a gradient that does not depend on p"
+    t = synth.ADAM_STEPS
+    c1, c2 = 1.0 - hp["beta1"] ** t, 1.0 - hp["beta2"] ** t
+    for lo in range(0, n, synth.C5_CHUNK):
+        hi = min(n, lo + synth.C5_CHUNK)
+        g1 = gr[lo:hi].astype(np.float64) / hp["grad_scale"]
+        p0 = p[lo:hi].astype(np.float64)
+        m_cf, v_cf = c1 * g1, c2 * g1 * g1
+        assert_fp32(host(mt[lo:hi]), m_cf, f"adam 350M closed-form exp_avg [{lo}, {hi})")
+        assert_fp32(host(vt[lo:hi]), v_cf, f"adam 350M closed-form exp_avg_sq [{lo}, {hi})")
+        p10 = host(pt[lo:hi])
+        pred = p0 - t * hp["lr"] * (g1 / (np.abs(g1) + hp["eps"]) + hp["weight_decay"] * p0)
+        top = np.maximum(np.abs(p0), np.abs(p10.astype(np.float64))).astype(np.float16)
+        tol = 5.0 * np.spacing(top).astype(np.float64) + 1e-7
+        err = np.abs(p10.astype(np.float64) - pred)
+        bad = err > tol
+        assert not bad.any(), (f"adam 350M closed-form params [{lo}, {hi}): {bad.sum()} off, "
+                               f"first at {lo + np.flatnonzero(bad)[0]}: {err[bad][0]} > {tol[bad][0]}")
 
 
 def test_adam_resume_bit_identical(ls):
