@@ -64,28 +64,30 @@ __device__ __forceinline__ void colsum_block_fold(float* partial, const float ac
     }
 }
 
-// out[c] = sum over the partial rows g = 0..ngroups-1 of partial[g][c]: 16
-// thread slices per column (slice s takes rows s, s+16, ...), then the 16
+// out[c] = sum over the partial rows g = 0..ngroups-1 of partial[g][c]: 32
+// thread slices per column (slice s takes rows s, s+32, ...), then the 32
 // slice sums in order.  ngroups == 0 writes zeros.  A block takes 32 columns,
-// so each partial row is read in whole 128-byte lines.
+// so each partial row is read in whole 128-byte lines; 1024 threads with 8
+// loads each (fewer loads per thread, more threads in flight, than 16 x 16).
 constexpr int kFinCols = 32;
-constexpr int kFinSlices = 16;
-static_assert(kFinSlices * 16 >= kMaxGroups, "16 loads per thread cover every partial row");
+constexpr int kFinSlices = 32;
+constexpr int kFinLoads = kMaxGroups / kFinSlices;
+static_assert(kFinSlices * kFinLoads >= kMaxGroups, "the loads of a thread cover every partial row");
 
 __global__ __launch_bounds__(kFinCols * kFinSlices) void colsum_finalize_kernel(half_t* out, const float* partial,
                                                                              uint32_t ngroups, uint32_t cols) {
     __shared__ float sums[kFinSlices][kFinCols];
     const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
     const uint32_t c = blockIdx.x * kFinCols + cl;
-    float v[16];
+    float v[kFinLoads];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kFinLoads; ++i) {
         const uint32_t g = sl + i * kFinSlices;
         v[i] = (c < cols && g < ngroups) ? partial[static_cast<size_t>(g) * cols + c] : 0.0f;
     }
     float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a += v[i];
+    for (int i = 0; i < kFinLoads; ++i) a += v[i];
     sums[sl][cl] = a;
     __syncthreads();
     if (sl == 0 && c < cols) {

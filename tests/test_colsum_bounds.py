@@ -20,7 +20,7 @@ from non_gemm_amd import _lib
 
 WAVE, WAVES = 64, 16                    # lanes per wave, waves per 1024-thread block
 SEG_VECS = 64                           # 16-byte vectors per column segment (512 columns)
-FIN_COLS, FIN_SLICES = 32, 16           # finalisation block: 32 columns x 16 slices, 16 loads per thread
+FIN_COLS, FIN_SLICES, FIN_LOADS = 32, 32, 8   # finalisation block: 32 columns x 32 slices, 8 loads per thread
 
 SHAPES = [(4096, 768), (4096, 3072), (8192, 1024), (8192, 4096), (200, 384), (333, 768), (129, 520),
           (1000, 4104), (7, 8), (1, 8), (37, 24), (4096, 2304), (8192, 3072), (5, 1000), (3, 13), (64, 64)]
@@ -79,7 +79,7 @@ def vec_kernel_accesses(rows, cols, groups, rpg):
 def finalize_accesses(cols, groups):
     """Partial-row elements colsum_finalize_kernel reads and d_bias elements it writes."""
     gx = -(-cols // FIN_COLS)
-    bx, sl, cl, i = np.meshgrid(np.arange(gx), np.arange(FIN_SLICES), np.arange(FIN_COLS), np.arange(16),
+    bx, sl, cl, i = np.meshgrid(np.arange(gx), np.arange(FIN_SLICES), np.arange(FIN_COLS), np.arange(FIN_LOADS),
                                 indexing="ij")
     c = bx * FIN_COLS + cl
     g = sl + i * FIN_SLICES
@@ -94,7 +94,7 @@ def finalize_accesses(cols, groups):
 @pytest.mark.parametrize("rows,cols", SHAPES)
 def test_column_sum_backward_stays_in_bounds(lib, rows, cols):
     groups, rpg, ws = geometry(lib, rows, cols)
-    assert groups <= FIN_SLICES * 16            # the finalisation's 16 loads per thread cover every row
+    assert groups <= FIN_SLICES * FIN_LOADS     # the finalisation's loads per thread cover every row
     part_elems = ws // 4
     reads, writes = finalize_accesses(cols, groups)
     assert reads.min() >= 0 and reads.max() < part_elems
