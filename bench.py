@@ -307,20 +307,40 @@ def chain_slice(inp, shape, s0, nseq):
             for k, v in inp.items()}
 
 
-def oracle_chain_pass(sl, shape, p, seed, eps):
-    """One pass of the oracle over every step of the chain, on a slice of it."""
+def oracle_chain_pass(sl, shape, p, seed, eps, times=None):
+    """One pass of the oracle over every step of the chain, on a slice of it.
+    times: a dict that collects each operator's seconds (summed over its calls)."""
     import oracle
     bits = 16
-    probs = oracle.softmax_fwd(sl["scores"])
-    a, l1, m1, r1 = oracle.bias_dropout_residual_layernorm(sl["attn_proj"], sl["attn_bias"], sl["residual"],
-                                                           sl["gamma1"], sl["beta1"], p, seed, 0, bits, eps)
-    oracle.bias_relu_dropout(sl["ffn_pre"], sl["ffn_bias1"], p, seed, 1, bits)
-    f, l2, m2, r2 = oracle.bias_dropout_residual_layernorm(sl["ffn_proj"], sl["ffn_bias2"], l1, sl["gamma2"],
-                                                           sl["beta2"], p, seed, 2, bits, eps)
-    oracle.layernorm_bwd(sl["grad_y2"], f, sl["gamma2"], m2, r2)
-    oracle.layernorm_bwd(sl["grad_y1"], a, sl["gamma1"], m1, r1)
+
+    def run(name, fn, *args):
+        t0 = time.perf_counter()
+        out = fn(*args)
+        if times is not None:
+            times[name] = times.get(name, 0.0) + time.perf_counter() - t0
+        return out
+    probs = run("softmax_fwd", oracle.softmax_fwd, sl["scores"])
+    a, l1, m1, r1 = run("bias_dropout_residual_layernorm", oracle.bias_dropout_residual_layernorm, sl["attn_proj"],
+                        sl["attn_bias"], sl["residual"], sl["gamma1"], sl["beta1"], p, seed, 0, bits, eps)
+    run("bias_relu_dropout", oracle.bias_relu_dropout, sl["ffn_pre"], sl["ffn_bias1"], p, seed, 1, bits)
+    f, l2, m2, r2 = run("bias_dropout_residual_layernorm", oracle.bias_dropout_residual_layernorm, sl["ffn_proj"],
+                        sl["ffn_bias2"], l1, sl["gamma2"], sl["beta2"], p, seed, 2, bits, eps)
+    run("layernorm_bwd", oracle.layernorm_bwd, sl["grad_y2"], f, sl["gamma2"], m2, r2)
+    run("layernorm_bwd", oracle.layernorm_bwd, sl["grad_y1"], a, sl["gamma1"], m1, r1)
     k = shape.seq
-    oracle.softmax_bwd(probs.reshape(-1, k), sl["grad_probs"].reshape(-1, k))
+    run("softmax_bwd", oracle.softmax_bwd, probs.reshape(-1, k), sl["grad_probs"].reshape(-1, k))
+
+
+def cpu_model():
+    """The host CPU's model string (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(shape, p, seed, eps, min_seconds=10.0, max_seconds=30.0):
@@ -333,14 +353,17 @@ def cpu_baseline(shape, p, seed, eps, min_seconds=10.0, max_seconds=30.0):
     T = nseq * shape.seq
     sl = chain_slice(synth.chain_inputs(shape, config=3), shape, 0, nseq)
     passes = 0
+    times = {}
     t0 = time.perf_counter()
     while True:
-        oracle_chain_pass(sl, shape, p, seed, eps)
+        oracle_chain_pass(sl, shape, p, seed, eps, times)
         passes += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or el + el / passes > max_seconds:
             break
-    _, _, bytes_per_pass = chain_bytes(T, shape.hidden, shape.ffn, shape.heads, shape.seq)
+    per, counts, bytes_per_pass = chain_bytes(T, shape.hidden, shape.ffn, shape.heads, shape.seq)
+    per_op = {op: {"ms_per_call": round(1e3 * sec / (passes * counts[op]), 3),
+                   "GB/s": round(per[op] * counts[op] * passes / sec / 1e9, 4)} for op, sec in times.items()}
     return {
         "value": round(bytes_per_pass * passes / el / 1e9, 4),
         "unit": "GB/s",
@@ -349,7 +372,10 @@ def cpu_baseline(shape, p, seed, eps, min_seconds=10.0, max_seconds=30.0):
         "sample": f"{passes} pass(es) of the full chain over {nseq} of 32 sequences ({T} of {shape.tokens} tokens), "
                   f"{el:.1f} s; NumPy float64, single thread",
         "tokens_per_s": round(T * passes / el, 1),
+        "per_operator": per_op,
         "host_cpus_available": len(os.sched_getaffinity(0)),
+        "host_cpu_count": os.cpu_count(),
+        "cpu_model": cpu_model(),
         "all_cores": cpu_baseline_sharded(shape, seconds=min_seconds / 2),
     }
 
@@ -923,10 +949,12 @@ def summarize_rows(fetch_csv, write_csv):
     print("\n".join(out))
 
 
-def summarize_trace(trace_csv, out_name, title, note, command):
+def summarize_trace(trace_csv, out_name, title, note, command, step_kernel=None):
     """Per-kernel duration statistics of the library's kernels from a
     rocprofv3 kernel trace (one row per kernel and grid size), written to
-    profiles/<out_name> with the command that made the trace."""
+    profiles/<out_name> with the command that made the trace.  step_kernel: a
+    kernel-name fragment that runs once per step; then the sum of kernel
+    durations per step is given too."""
     import csv
     import statistics
     groups = {}
@@ -948,6 +976,11 @@ def summarize_trace(trace_csv, out_name, title, note, command):
                              f"{statistics.median(v):.2f} | {q(0.9):.2f} | {v[0]:.2f} | {v[-1]:.2f} | "
                              f"{100 * sum(v) / total:.1f} |"))
     rows.sort(reverse=True)
+    if step_kernel:
+        steps = sum(len(v) for (name, _), v in groups.items() if step_kernel in name)
+        if steps:
+            note += (f"\n\nSum of the library's kernel durations per step: {total / steps:.2f} us ({steps} steps "
+                     f"traced; the step's own wall time, dispatch gaps included, is the bench line's ms_per_step).")
     out = [f"# rocprofv3 kernel statistics: {title}", "", note, "",
            "Command (from the repository root on the MI355X machine; R = repository root, OUT = an output folder):",
            "", "```", command, "```", "",
@@ -975,7 +1008,7 @@ def stored_traffic():
 
 def transformer_big_chain(torch, lib, check, cap_stream, side, p, seed, eps, nsets=3, reps=20):
     """The Transformer-big layer (8192 tokens, hidden 1024, 16 heads, FFN 4096)
-    through the same 11 launches plus the embedding forward and backward
+    through the same calls as the BERT-base step plus the embedding forward and backward
     (vocabulary 32768, Zipf ids, fp32 gradient accumulated), one HIP graph per
     rotated buffer set (about 0.9 GB each)."""
     import numpy as np
@@ -1137,7 +1170,8 @@ def main():
                             "than in the untraced step (compare p10 with the live figures in the bench line).",
                             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/prof_trace -o trace "
                             "--output-format csv -- python3 $R/bench.py --steps 200 --warmup 20 --no-cpu --no-extra "
-                            "--no-info\npython $R/bench.py --summarize-trace chain $OUT/prof_trace/trace_kernel_trace.csv")
+                            "--no-info\npython $R/bench.py --summarize-trace chain $OUT/prof_trace/trace_kernel_trace.csv",
+                            step_kernel="ln_bwd_finalize_kernel")
         else:
             summarize_trace(path, "other_rows_kernel_stats.md", "rows outside the chain",
                             "Elementwise backwards and bias + Q/K/V split at the BERT-base shapes; the chain's kernels "
