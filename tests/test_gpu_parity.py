@@ -1182,6 +1182,12 @@ def test_graph_replay_matches_eager(ls):
     ids = dev(g.integers(0, 500, size=(2, 128)).astype(np.int32))
     dE = torch.empty((500, H), dtype=torch.float32, device="cuda")
     edy = dev(synth.normal16(g, (256, H), 1.0))
+    # the fused block and the LayerNorm backward as its input call plus the
+    # batched parameter call (two LayerNorms' workspaces)
+    out.update({k: torch.empty_like(x) for k in ("z2", "y2", "dx2", "dx3")})
+    mean2, rstd2 = torch.empty(T, device="cuda"), torch.empty(T, device="cuda")
+    pg = {k: torch.empty(H, dtype=torch.float16, device="cuda") for k in ("dg2", "db2", "dg3", "db3")}
+    ws2, ws3 = torch.empty_like(ws), torch.empty_like(ws)
 
     def step():
         ls.bias_dropout_residual(x, b, r, 0.1, SEED, 0, out=out["z"])
@@ -1191,10 +1197,15 @@ def test_graph_replay_matches_eager(ls):
         ls.softmax_fwd(sc, y=out["s"])
         ls.softmax_bwd(out["s"], sc, dx=out["ds"])
         ls.embedding_bwd(ids, edy, dE, 16.0, 0.1, SEED, 3, zero_first=True)
+        ls.bias_dropout_residual_layernorm(x, b, r, gm, bt, 0.1, SEED, 2, 1e-5, z=out["z2"], y=out["y2"],
+                                           mean=mean2, rstd=rstd2)
+        ls.layernorm_bwd_input(dy, out["z2"], gm, mean2, rstd2, ws2, dx=out["dx2"])
+        ls.layernorm_bwd_input(out["y2"], out["z"], gm, mean, rstd, ws3, dx=out["dx3"])
+        ls.layernorm_bwd_params_batched([(T, H, ws2, pg["dg2"], pg["db2"]), (T, H, ws3, pg["dg3"], pg["db3"])])
 
     def snap():
         torch.cuda.synchronize()
-        return [t.clone() for t in (*out.values(), mean, rstd, dg, db, dE)]
+        return [t.clone() for t in (*out.values(), mean, rstd, dg, db, mean2, rstd2, *pg.values(), dE)]
 
     step()
     ref = snap()
@@ -1203,7 +1214,7 @@ def test_graph_replay_matches_eager(ls):
     with torch.cuda.graph(graph, stream=stream):
         step()
     for rep in range(3):
-        for t in (*out.values(), mean, rstd, dg, db, dE):
+        for t in (*out.values(), mean, rstd, dg, db, mean2, rstd2, *pg.values(), dE):
             t.fill_(7)                         # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
