@@ -1136,9 +1136,12 @@ def warm_chain_us(torch, s, cap_stream, check, side, reps=100):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sets", type=int, default=12, help="rotated buffer sets (cold-cache measurement)")
+    ap.add_argument("--sample-every", type=int, default=0,
+                    help="every Nth timed step runs the dominant kernel between its own events "
+                         "(default: about 25-32 samples over the timed steps)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the embedding / Adam rows")
     ap.add_argument("--eager", action="store_true",
@@ -1238,7 +1241,10 @@ def main():
     stream = torch.cuda.current_stream()
     S = stream.cuda_stream
     dom = [(s.launches[dom_idx][2], s.launches[dom_idx][3][:-1] + (S,)) for s in sets]
-    SAMPLE = 8
+    # A sampled step (two graphs around a direct launch) costs about 1 us more
+    # than a whole-step graph, so only every SAMPLE-th step is one: enough
+    # samples for the kernel's mean, little of that cost in the step time.
+    SAMPLE = args.sample_every if args.sample_every > 0 else max(1, min(32, args.steps // 24))
 
     def step(i, ev=None):
         s = sets[i % len(sets)]
@@ -1378,6 +1384,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": stored_traffic(), "algorithmic_bytes": dom_bytes,
                      "avg_duration_us": round(dom_us, 3),
+                     "samples": len(range(0, K, SAMPLE)), "sample_every": SAMPLE,
                      # the whole operator (row kernel, then its parameter finalisation on the same stream),
                      # from the cold per-operator timing
                      "op_level": None if DOMINANT not in kernels else {
