@@ -285,7 +285,8 @@ int ls_layernorm_bwd_noalloc(void* dx, void* dgamma, void* dbeta, const void* dy
  * gradients off the critical path: only the input gradient dx feeds the
  * rest of the backward pass, while dgamma / dbeta wait for the optimizer, so
  * the finalisation may run on another stream (ordered after the input call
- * by an event) while the next operators proceed.
+ * by an event) while the next operators proceed, or later, together with
+ * other LayerNorms' (ls_layernorm_bwd_params_batched).
  * ls_layernorm_bwd_input: dx, and the fixed-order per-block column partials
  * plus their count into workspace (arguments and errors as ls_layernorm_bwd;
  * rows == 0 launches nothing).
@@ -312,7 +313,8 @@ int ls_layernorm_bwd_params(void* dgamma, void* dbeta, int64_t rows, int64_t hid
  * hold its own input call's partials, complete and not overwritten.
  * The arrays are host arrays of `count` entries; up to 16 jobs share a
  * launch (more take several).  Jobs with hidden == 0 are skipped; rows == 0
- * writes zeros without reading that job's workspace.  Every job is checked
+ * writes zeros without reading that job's workspace.  The jobs' outputs must
+ * not overlap one another (nor any workspace).  Every job is checked
  * before anything is launched; the first failing job's error is returned
  * (the message names the job) and nothing runs.  count == 0 launches nothing.
  * Errors: LS_ERR_PARAM (count < 0, misaligned workspace), LS_ERR_NULL (a null
