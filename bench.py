@@ -87,14 +87,25 @@ def chain_bytes(tokens, hidden, ffn, heads, seq, fused=True):
 DOMINANT_SOURCES = ("layernorm.hip", "ls_common.hpp")
 
 
+def code_text(src):
+    """C++ source without its comments and blank-line or indentation changes:
+    what the compiler sees of it, so that a comment edit does not make
+    stored counters look stale.  (String literals are not parsed; a "//"
+    inside one cuts the rest of that line for hashing, the same way each time.)"""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).strip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash():
-    """Hash of the dominant kernel's sources, used to tell whether stored counters are stale."""
+    """Hash of the dominant kernel's sources (their code, not their comments),
+    used to tell whether stored counters are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "non_gemm_amd", "csrc")
     for name in DOMINANT_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,15 +4,18 @@
 // and S2 = sum d^2 over its elements, d = x - K with K the row's first
 // element; the two sums travel through the same DPP/swizzle reduction, so
 // the row needs a single cross-lane pass instead of "mean first, then
-// variance":  mean = K + S1/H, var = S2/H - (S1/H)^2 (clamped at 0).
+// variance":  mean = K + S1/H, var = S2/H - (S1/H)^2 (clamped at 0).  The
+// same kernel (FUSED) also forms z = residual + Dropout(x + bias) chunk by
+// chunk, stores it, and normalises it from registers: the sub-layer output
+// block in one launch.
 //
 // Backward: the two row sums A = sum gamma*dy and B = sum gamma*dy*xhat are
 // likewise reduced together, then dx = rstd * (gamma*dy - A/H - xhat*B/H).
 // dgamma / dbeta are column sums over all rows: every block keeps per-lane
 // fp32 column accumulators in registers over the rows it owns, folds them
 // across its waves in a fixed order through LDS, and writes one partial row
-// per block; a second kernel sums the partial rows in a fixed order, so the
-// result is bit-reproducible.
+// per block; a second kernel sums the partial rows in a fixed order (for up
+// to 16 LayerNorms in one launch), so the result is bit-reproducible.
 //
 // Rows are mapped to aligned groups of LPR lanes (LPR = 8..64), each lane
 // holding NCH chunks of CW consecutive elements (CW = 8: one 16-byte access
