@@ -35,3 +35,21 @@ def test_sharded_oracle_baseline_runs_every_worker():
     per = -(-nseq // min(len(os.sched_getaffinity(0)), nseq))          # sequences per worker
     assert r["cores"] == len(range(0, nseq, per))
     assert r["value"] > 0 and r["tokens_per_s"] > 0
+
+
+def test_counter_staleness_hash_ignores_comments_only():
+    """The stored counters stay valid across comment edits of the dominant
+    kernel's sources and become stale on any code edit."""
+    code = "int f(int a) {  // add one\n    return a + 1;  /* done */\n}\n"
+    assert bench.code_text(code) == bench.code_text("// header\nint f(int a) {\n\n  return a + 1;\n}\n")
+    assert bench.code_text(code) != bench.code_text(code.replace("a + 1", "a + 2"))
+    assert bench.code_text("/* a\n multi-line\n comment */ x = 1;") == "x = 1;"
+
+
+def test_cpu_baseline_reports_each_operator():
+    r = bench.cpu_baseline(synth.C3, synth.DROPOUT_P, synth.DROPOUT_SEED, synth.LN_EPS, min_seconds=0.1,
+                           max_seconds=5.0)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    _, counts, _ = bench.chain_bytes(512, synth.C3.hidden, synth.C3.ffn, synth.C3.heads, synth.C3.seq)
+    assert set(r["per_operator"]) == set(counts)
+    assert all(v["ms_per_call"] > 0 and v["GB/s"] > 0 for v in r["per_operator"].values())
