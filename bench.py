@@ -388,7 +388,59 @@ def cpu_baseline(shape, p, seed, eps, min_seconds=10.0, max_seconds=30.0):
         "host_cpu_count": os.cpu_count(),
         "cpu_model": cpu_model(),
         "all_cores": cpu_baseline_sharded(shape, seconds=min_seconds / 2),
+        "other_configs": cpu_baseline_other(p, seed, eps, seconds=min(2.0, min_seconds / 5)),
     }
+
+
+def cpu_baseline_other(p, seed, eps, seconds=2.0):
+    """The oracle (single thread) on bounded samples of the other configs:
+    the Transformer-big chain over 1 of its 32 sequences, the embedding
+    forward and backward over the same 256 tokens, and one Adam step over one
+    8M-parameter chunk of the 350M workspace; each repeated for `seconds`."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    def repeat(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return n, el
+    out = {}
+    shape = synth.C4
+    T, H = shape.seq, shape.hidden
+    sl = chain_slice(synth.chain_inputs(shape, config=4), shape, 0, 1)
+    n, el = repeat(lambda: oracle_chain_pass(sl, shape, p, seed, eps))
+    _, _, b = chain_bytes(T, H, shape.ffn, shape.heads, shape.seq)
+    out["transformer_big_chain"] = {"GB/s": round(b * n / el / 1e9, 4), "tokens_per_s": round(T * n / el, 1),
+                                    "sample": f"{n} passes over 1 of {shape.batch} sequences ({T} tokens)"}
+    e = synth.embedding_inputs()
+    ids, dy = e["ids"][:1], e["grad_out"][:T]
+    distinct = int(np.unique(ids).size)
+    bits = 16                                   # the dropout decision fields, as in oracle_chain_pass
+    n, el = repeat(lambda: oracle.embedding_fwd(ids, e["tok_emb"], e["pos_emb"], e["scale"], p, seed,
+                                                synth.SITE_EMBEDDING, bits))
+    nb = 4 * T + 2 * H * distinct + 2 * H * T + 2 * T * H
+    out["embedding_fwd"] = {"GB/s": round(nb * n / el / 1e9, 4), "tokens_per_s": round(T * n / el, 1),
+                            "sample": f"{n} passes over {T} tokens ({distinct} distinct ids)"}
+    n, el = repeat(lambda: oracle.embedding_bwd(ids, dy, shape.vocab, e["scale"], p, seed, synth.SITE_EMBEDDING,
+                                                bits))
+    nb = 4 * T + 2 * T * H + 8 * H * distinct
+    out["embedding_bwd"] = {"GB/s": round(nb * n / el / 1e9, 4), "tokens_per_s": round(T * n / el, 1),
+                            "sample": f"{n} passes over {T} tokens ({distinct} distinct ids)"}
+    pc, gc = synth.adam_chunk(0)
+    m0, v0 = np.zeros(pc.size, np.float32), np.zeros(pc.size, np.float32)
+    hp = synth.ADAM_HYPER
+    n, el = repeat(lambda: oracle.adam_workspace_step(pc, gc, m0, v0, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                                      hp["weight_decay"], 1, hp["grad_scale"], hp["decoupled_wd"]))
+    out["adam_workspace_step"] = {"GB/s": round(22 * pc.size * n / el / 1e9, 4),
+                                  "params_per_s": round(pc.size * n / el, 1),
+                                  "sample": f"{n} steps over one {pc.size}-parameter chunk of the 350M workspace"}
+    return out
 
 
 def cpu_baseline_sharded(shape, seconds):

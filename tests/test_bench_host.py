@@ -53,3 +53,6 @@ def test_cpu_baseline_reports_each_operator():
     _, counts, _ = bench.chain_bytes(512, synth.C3.hidden, synth.C3.ffn, synth.C3.heads, synth.C3.seq)
     assert set(r["per_operator"]) == set(counts)
     assert all(v["ms_per_call"] > 0 and v["GB/s"] > 0 for v in r["per_operator"].values())
+    other = r["other_configs"]
+    assert set(other) == {"transformer_big_chain", "embedding_fwd", "embedding_bwd", "adam_workspace_step"}
+    assert all(v["GB/s"] > 0 for v in other.values())
