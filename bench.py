@@ -626,6 +626,49 @@ def extra_rows(torch, ops, eager=False):
     torch.cuda.empty_cache()
     out["transformer_big_kernels"] = c4
 
+    # The two parity configs, timed for the record (launch- and cache-bound:
+    # no bandwidth target): the tiny chain at 128 x 256 (the fused block, then
+    # the LayerNorm backward's input and parameter calls) and the attention
+    # softmax at [8, 12, 128, 128] with per-sequence key lengths, plain and
+    # causal.  (Left out of the counter runs: their kernels share names with
+    # the rows above.)
+    if not eager:
+        S1 = synth.C1
+        T1, H1 = S1.tokens, S1.hidden
+        per1, _, _ = chain_bytes(T1, H1, S1.ffn, S1.heads, S1.seq)
+        gm1, bt1, b1 = rnd(H1).abs() + 0.5, rnd(H1), rnd(H1)
+        ws1n = ops.layernorm_bwd_workspace_bytes(T1, H1)
+        sets1 = [{"x": rnd(T1, H1), "r": rnd(T1, H1), "dy": rnd(T1, H1), "z": emp(T1, H1), "y": emp(T1, H1),
+                  "dx": emp(T1, H1), "m": emp(T1, dt=torch.float32), "s": emp(T1, dt=torch.float32),
+                  "dg": emp(H1), "db": emp(H1), "ws": emp(ws1n, dt=torch.uint8)} for _ in range(64)]
+        calls = []
+        for t in sets1:
+            calls += [lambda t=t: ops.bias_dropout_residual_layernorm(t["x"], b1, t["r"], gm1, bt1, p, seed, 0,
+                                                                      synth.LN_EPS, z=t["z"], y=t["y"], mean=t["m"],
+                                                                      rstd=t["s"]),
+                      lambda t=t: ops.layernorm_bwd_input(t["dy"], t["z"], gm1, t["m"], t["s"], t["ws"], dx=t["dx"]),
+                      lambda t=t: ops.layernorm_bwd_params(T1, H1, t["ws"], dgamma=t["dg"], dbeta=t["db"])]
+        us = 3 * cold(calls)
+        nb = (per1["bias_dropout_residual_layernorm"] + per1["layernorm_bwd_input"] +
+              per1["layernorm_bwd_params"])
+        out["tiny_chain"] = row(f"[{T1},{H1}]: fused block, LayerNorm backward input and parameter calls", us, nb,
+                                calls_per_chain=3, tokens_per_s=round(T1 / (us * 1e-6), 1))
+        del sets1, calls
+        inp2 = synth.softmax_inputs()
+        kl = d(inp2["key_lengths"])
+        e2 = int(np.prod(synth.C2_SHAPE))
+        sets2 = [(d(inp2["scores"]), emp(*synth.C2_SHAPE), d(inp2["grad_out"]), emp(*synth.C2_SHAPE))
+                 for _ in range(16)]
+        for causal in (False, True):
+            key = "attention_softmax_fwd" + ("_causal" if causal else "")
+            out[key] = row(f"{list(synth.C2_SHAPE)}, per-sequence key lengths" + (", causal" if causal else ""),
+                           cold([lambda s=s, c=causal: ops.softmax_fwd(s[0], kl, c, y=s[1]) for s in sets2]), 4 * e2)
+        out["attention_softmax_bwd"] = row(f"{list(synth.C2_SHAPE)}",
+                                           cold([lambda s=s: ops.softmax_bwd(s[1], s[2], dx=s[3]) for s in sets2]),
+                                           6 * e2)
+        del sets2
+        torch.cuda.empty_cache()
+
     # Bias + Q/K/V head split and its backward, C3 attention shape
     B, L, NH = synth.C3.batch, synth.C3.seq, synth.C3.heads
     H3 = 3 * H
