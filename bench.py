@@ -42,8 +42,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 # The dominant kernel: the one with the largest share of the chain's time --
-# the LayerNorm backward's row kernel, launched twice per step.  (The largest
-# single launch, bias+ReLU+dropout, is reported beside it.)
+# the LayerNorm backward's row kernel, launched twice per step; the fused
+# block's kernel (also twice per step) takes as much time within a few
+# percent, at a higher fraction of its roofline, so the lower one is reported.
+# (The largest single launch, bias+ReLU+dropout, is reported beside it.)
 DOMINANT = "layernorm_bwd"
 DOMINANT_SHAPE = "[4096,768]"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "layernorm_bwd_4096x768_counters.json")

@@ -326,11 +326,13 @@ __global__ __launch_bounds__(BT) void ln_fwd_kernel(half_t* y, float* mean, floa
 // Blocks of 4..16 waves (sized so that ~one block per CU covers the rows);
 // each wave walks its rows, every load of a row issued before the first
 // wait.  (A prefetch of the next row into a second register set measured
-// slower: it costs the registers that a 16-wave block needs.)  After the
-// rows, the per-lane column
-// accumulators are folded: first across the row groups inside each wave
-// (shuffles), then across waves through one LDS slot per wave, and the block
-// writes its partial row [2h] = (dgamma part, dbeta part).
+// slower: it costs the registers that a 16-wave block needs.)  Once a wave
+// has accumulated its last row, its per-lane column accumulators are folded
+// across the row groups inside the wave (shuffles) and parked in the wave's
+// LDS slot; after a barrier the slots are summed in wave order, and the block
+// writes its partial row [2h] = (dgamma part, dbeta part).  The grid never
+// exceeds the number of row groups, so every block, and every wave in it,
+// takes at least one pass of the row loop, and each wave parks exactly once.
 // Waves per block by register budget: 16 when a lane holds <= 16 elements
 // (<= 128 VGPRs), 8 up to 32 elements, 4 beyond (one wave per SIMD, up to 512
 // VGPRs, so the largest rows do not spill); the wave slots of the column fold
@@ -436,6 +438,49 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
             rs = ok ? rstd[row] : 0.0f;
         }
     };
+    // Parks this wave's column sums in its LDS slot.  Called right after the
+    // last row's accumulation, so the LDS writes overlap that row's dx work
+    // (0.1 us per call and 0.3 us per BERT-base step faster than after it).
+    auto park = [&]() {
+        if constexpr (!kTwoPass) {
+            // Fold the RPW row groups of this wave (lanes l, l+LPR, ... own the same columns).
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int k = 0; k < CW; ++k)
+#pragma unroll
+                    for (int o = LPR; o < kWave; o <<= 1) {
+                        acc_g[j][k] += __shfl_xor(acc_g[j][k], o);
+                        acc_b[j][k] += __shfl_xor(acc_b[j][k], o);
+                    }
+            // Every wave parks its column sums in its own LDS slot [wave][2h]; after
+            // one barrier each thread sums whole columns over the slots in wave order
+            // and writes the block's partial row.  The order is fixed, so the sums are.
+            if (sub == 0) {
+                float* mine = lds + static_cast<size_t>(wave) * 2 * h;
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) {
+                    const uint32_t c = (l + j * LPR) * CW;
+                    if (c < h) {
+                        if constexpr (CW == 8) {      // two 16-byte LDS stores per half
+                            float4v* pg = reinterpret_cast<float4v*>(mine + c);
+                            float4v* pb = reinterpret_cast<float4v*>(mine + h + c);
+                            pg[0] = float4v{acc_g[j][0], acc_g[j][1], acc_g[j][2], acc_g[j][3]};
+                            pg[1] = float4v{acc_g[j][4], acc_g[j][5], acc_g[j][6], acc_g[j][7]};
+                            pb[0] = float4v{acc_b[j][0], acc_b[j][1], acc_b[j][2], acc_b[j][3]};
+                            pb[1] = float4v{acc_b[j][4], acc_b[j][5], acc_b[j][6], acc_b[j][7]};
+                        } else {
+#pragma unroll
+                            for (int k = 0; k < CW; ++k) {
+                                mine[c + k] = acc_g[j][k];
+                                mine[h + c + k] = acc_b[j][k];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    };
     if constexpr (kTwoPass) {
         // Element-wise rows longer than 2048: each row is read twice, in
         // batches of kB elements per lane -- sums, then dx from the caches --
@@ -536,6 +581,7 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
                 acc_b[j][k] += fd[k];
             }
         }
+        if (r0 + stride >= rows) park();  // the wave's last row: sums complete
         sa = group_sum<LPR>(sa);          // the two row sums, reduced together
         sb = group_sum<LPR>(sb);
         const float ca = sa * inv_h, cb = sb * inv_h;
@@ -553,45 +599,6 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
                     for (int k = 0; k < CW; ++k)
                         o[k] = rs * (fg[k] * fd[k] - fmaf((fx[k] - mu) * rs, cb, ca));
                     Chunk<CW>::store(dx, base + c, o);
-                }
-            }
-        }
-    }
-    }
-
-    if constexpr (!kTwoPass) {
-    // Fold the RPW row groups of this wave (lanes l, l+LPR, ... own the same columns).
-#pragma unroll
-    for (int j = 0; j < NCH; ++j)
-#pragma unroll
-        for (int k = 0; k < CW; ++k)
-#pragma unroll
-            for (int o = LPR; o < kWave; o <<= 1) {
-                acc_g[j][k] += __shfl_xor(acc_g[j][k], o);
-                acc_b[j][k] += __shfl_xor(acc_b[j][k], o);
-            }
-    // Every wave parks its column sums in its own LDS slot [wave][2h]; after
-    // one barrier each thread sums whole columns over the slots in wave order
-    // and writes the block's partial row.  The order is fixed, so the sums are.
-    if (sub == 0) {
-        float* mine = lds + static_cast<size_t>(wave) * 2 * h;
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const uint32_t c = (l + j * LPR) * CW;
-            if (c < h) {
-                if constexpr (CW == 8) {      // two 16-byte LDS stores per half
-                    float4v* pg = reinterpret_cast<float4v*>(mine + c);
-                    float4v* pb = reinterpret_cast<float4v*>(mine + h + c);
-                    pg[0] = float4v{acc_g[j][0], acc_g[j][1], acc_g[j][2], acc_g[j][3]};
-                    pg[1] = float4v{acc_g[j][4], acc_g[j][5], acc_g[j][6], acc_g[j][7]};
-                    pb[0] = float4v{acc_b[j][0], acc_b[j][1], acc_b[j][2], acc_b[j][3]};
-                    pb[1] = float4v{acc_b[j][4], acc_b[j][5], acc_b[j][6], acc_b[j][7]};
-                } else {
-#pragma unroll
-                    for (int k = 0; k < CW; ++k) {
-                        mine[c + k] = acc_g[j][k];
-                        mine[h + c + k] = acc_b[j][k];
-                    }
                 }
             }
         }
