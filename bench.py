@@ -953,6 +953,13 @@ def other_rows_bytes():
     for k in ("bias_dropout_residual", "bias_dropout_residual_layernorm", "bias_relu_dropout", "layernorm_fwd",
               "layernorm_bwd", "softmax_fwd", "softmax_bwd"):
         out[f"{k} C4"] = per4[k]
+    S1 = synth.C1
+    per1, _, _ = chain_bytes(S1.tokens, S1.hidden, S1.ffn, S1.heads, S1.seq)
+    out["tiny_chain C1 (3 calls)"] = (per1["bias_dropout_residual_layernorm"] + per1["layernorm_bwd_input"] +
+                                      per1["layernorm_bwd_params"])
+    e2 = int(np.prod(synth.C2_SHAPE))
+    out["attention_softmax_fwd C2"] = 4 * e2
+    out["attention_softmax_bwd C2"] = 6 * e2
     return out
 
 
@@ -1160,11 +1167,13 @@ def transformer_big_chain(torch, lib, check, cap_stream, side, p, seed, eps, nse
     return out
 
 
-def attainable(torch, lib, check, cap_stream, dom_bytes):
+def attainable(torch, lib, check, cap_stream, dom_bytes, sizes=None):
     """Bandwidth the device reaches with the operators' access pattern: the
     library's reference copy and read kernels over 1 GiB buffers, and a copy
     moving the dominant kernel's byte count, rotated over enough buffers to
-    stay out of the 256 MB Infinity Cache."""
+    stay out of the 256 MB Infinity Cache.  sizes ({name: bytes}): a cold
+    copy of each kernel's own byte count (half read, half written), the
+    reference its time is compared with."""
     def rate(pairs, fn, moved, reps=10):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap_stream):
@@ -1197,6 +1206,19 @@ def attainable(torch, lib, check, cap_stream, dom_bytes):
     out["copy_dominant_bytes"] = 2 * half
     del pairs
     torch.cuda.empty_cache()
+    if sizes:
+        measured, table = {}, {}
+        for name, nbytes in sizes.items():
+            half = (nbytes // 2) // 16 * 16
+            if half not in measured:
+                n_pairs = max(2, -(-int(1.5e9) // (2 * half)))
+                pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+                          torch.ones(half, dtype=torch.uint8, device="cuda")) for _ in range(n_pairs)]
+                measured[half] = rate(pairs, lib.ls_probe_copy, 2 * half)[1]
+                del pairs
+                torch.cuda.empty_cache()
+            table[name] = {"bytes": nbytes, "copy_us": measured[half]}
+        out["same_size_copy"] = table
     return out
 
 
@@ -1458,7 +1480,12 @@ def main():
     torch.cuda.empty_cache()
     variants = None if args.no_info else step_variants(torch, lib, check, cap_stream, p, seed, eps,
                                                        nsets=args.sets)
-    reach = None if args.no_info else attainable(torch, lib, check, cap_stream, dom_bytes)
+    copy_sizes = {**{f"{k} C3": per[k] for k in kernels}, **other_rows_bytes()}
+    reach = None if args.no_info else attainable(torch, lib, check, cap_stream, dom_bytes, copy_sizes)
+    if reach is not None:
+        for k in kernels:
+            kernels[k]["pct_of_same_size_copy"] = round(
+                100 * reach["same_size_copy"][f"{k} C3"]["copy_us"] / kernels[k]["us"], 1)
     big = None if args.no_info else transformer_big_chain(torch, lib, check, cap_stream, side, p, seed, eps)
 
     extra = None if args.no_extra else extra_rows(torch, ops)
