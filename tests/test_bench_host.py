@@ -56,3 +56,13 @@ def test_cpu_baseline_reports_each_operator():
     other = r["other_configs"]
     assert set(other) == {"transformer_big_chain", "embedding_fwd", "embedding_bwd", "adam_workspace_step"}
     assert all(v["GB/s"] > 0 for v in other.values())
+
+
+def test_same_size_copy_covers_every_row():
+    """Every row whose traffic the counters summary reports also gets a
+    same-size copy reference (the bench passes other_rows_bytes() to it)."""
+    rows = bench.other_rows_bytes()
+    for row, _, _, _ in bench.ROW_KERNELS:
+        assert row in rows and rows[row] > 0
+    for key in ("tiny_chain C1 (3 calls)", "attention_softmax_fwd C2", "attention_softmax_bwd C2"):
+        assert rows[key] > 0
