@@ -66,7 +66,10 @@ __device__ __forceinline__ void colsum_block_fold(float* partial, const float ac
 
 // out[c] = sum over the partial rows g = 0..ngroups-1 of partial[g][c]: 32
 // thread slices per column (slice s takes rows s, s+32, ...), then the 32
-// slice sums in order.  ngroups == 0 writes zeros.  A block takes 32 columns,
+// slice sums in order.  ngroups == 0 writes zeros.  Every load is issued
+// at an index clamped into the buffer and masked after it arrives: under a
+// per-lane condition the compiler waited for the first load before issuing
+// the rest.  A block takes 32 columns,
 // so each partial row is read in whole 128-byte lines; 1024 threads with 8
 // loads each (fewer loads per thread, more threads in flight, than 16 x 16).
 constexpr int kFinCols = 32;
@@ -80,11 +83,19 @@ __global__ __launch_bounds__(kFinCols * kFinSlices) void colsum_finalize_kernel(
     const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
     const uint32_t c = blockIdx.x * kFinCols + cl;
     float v[kFinLoads];
+    if (ngroups) {
+        const uint32_t cc = c < cols ? c : cols - 1;
 #pragma unroll
-    for (int i = 0; i < kFinLoads; ++i) {
-        const uint32_t g = sl + i * kFinSlices;
-        v[i] = (c < cols && g < ngroups) ? partial[static_cast<size_t>(g) * cols + c] : 0.0f;
+        for (int i = 0; i < kFinLoads; ++i) {
+            const uint32_t g = sl + i * kFinSlices;
+            v[i] = partial[static_cast<size_t>(g < ngroups ? g : ngroups - 1) * cols + cc];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kFinLoads; ++i) v[i] = 0.0f;
     }
+#pragma unroll
+    for (int i = 0; i < kFinLoads; ++i) v[i] = (c < cols && sl + i * kFinSlices < ngroups) ? v[i] : 0.0f;
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < kFinLoads; ++i) a += v[i];

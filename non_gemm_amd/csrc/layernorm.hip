@@ -646,11 +646,12 @@ constexpr int kFinLoads = kMaxBwdBlocks / kFinSlices;
 
 // Finalisations of up to kFinMaxJobs LayerNorms in one launch (a layer's or
 // a model's LayerNorms, whose parameter gradients wait for the optimizer):
-// job j takes blocks [first_block[j], first_block[j + 1]).  Each job's
-// partial-row count comes from the workspace header its row kernel wrote,
-// clamped to max_blocks (the count the workspace is sized for), so a stale
-// header cannot send a read past the partial rows; max_blocks == 0 (no rows)
-// writes zeros without reading the workspace.
+// job j takes blocks [first_block[j], first_block[j + 1]).  A thread loads
+// its partial rows up to max_blocks (the count the workspace is sized for,
+// indices clamped into it) together with the workspace header, and only then
+// drops the rows past the header's count (clamped to max_blocks, so a stale
+// header cannot widen the sum): no load waits for the header.  max_blocks == 0
+// (no rows) writes zeros without reading the workspace.
 constexpr int kFinMaxJobs = 16;
 struct FinJobs {
     uint32_t count;
@@ -669,16 +670,25 @@ __global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
     while (j + 1 < jobs.count && blockIdx.x >= jobs.first_block[j + 1]) ++j;
     const uint32_t h = jobs.h[j], max_blocks = jobs.max_blocks[j];
     const float* partial = jobs.partial[j];
-    const uint32_t nblocks = max_blocks ? min(jobs.header[j][0], max_blocks) : 0u;
     const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
     const uint32_t c = (blockIdx.x - jobs.first_block[j]) * kFinCols + cl;
     const uint32_t w = 2 * h;
     float v[kFinLoads];
+    uint32_t nblocks = 0;
+    if (max_blocks) {
+        const uint32_t cc = c < w ? c : w - 1;
 #pragma unroll
-    for (int i = 0; i < kFinLoads; ++i) {
-        const uint32_t b = sl + i * kFinSlices;
-        v[i] = (c < w && b < nblocks) ? partial[static_cast<size_t>(b) * w + c] : 0.0f;
+        for (int i = 0; i < kFinLoads; ++i) {
+            const uint32_t b = sl + i * kFinSlices;
+            v[i] = partial[static_cast<size_t>(b < max_blocks ? b : max_blocks - 1) * w + cc];
+        }
+        nblocks = min(jobs.header[j][0], max_blocks);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kFinLoads; ++i) v[i] = 0.0f;
     }
+#pragma unroll
+    for (int i = 0; i < kFinLoads; ++i) v[i] = (c < w && sl + i * kFinSlices < nblocks) ? v[i] : 0.0f;
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < kFinLoads; ++i) a += v[i];

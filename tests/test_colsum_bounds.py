@@ -83,8 +83,9 @@ def finalize_accesses(cols, groups):
                                 indexing="ij")
     c = bx * FIN_COLS + cl
     g = sl + i * FIN_SLICES
-    ok = (c < cols) & (g < groups)
-    reads = g[ok] * cols + c[ok]
+    # every thread loads at clamped indices (the values past the rows or
+    # columns are masked after they arrive); with no groups nothing is read
+    reads = (np.minimum(g, groups - 1) * cols + np.minimum(c, cols - 1)).ravel() if groups else np.zeros(0, int)
     # slice 0 of each block writes its 32 columns
     writes = (np.arange(gx)[:, None] * FIN_COLS + np.arange(FIN_COLS)[None, :]).ravel()
     writes = writes[writes < cols]
@@ -97,7 +98,7 @@ def test_column_sum_backward_stays_in_bounds(lib, rows, cols):
     assert groups <= FIN_SLICES * FIN_LOADS     # the finalisation's loads per thread cover every row
     part_elems = ws // 4
     reads, writes = finalize_accesses(cols, groups)
-    assert reads.min() >= 0 and reads.max() < part_elems
+    assert reads.size and reads.min() >= 0 and reads.max() < part_elems
     assert writes.min() >= 0 and writes.max() < cols
     assert np.unique(writes).size == cols       # every d_bias element written exactly by one thread
     if cols % 8 == 0:
