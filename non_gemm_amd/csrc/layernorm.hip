@@ -364,9 +364,8 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
     // The partial-row count, for the finalisation (which may run as a
     // separate call).
     if (blockIdx.x == 0 && threadIdx.x == 0) header[0] = gridDim.x;
-    // Element-wise rows of up to 2048: one register per element and clamped
-    // unconditional loads; longer ones are read twice (kTwoPass).
-    constexpr bool kClamped = CW == 1 && NCH <= 32;
+    // Element-wise rows of up to 2048 hold one register per element; longer
+    // ones are read twice (kTwoPass).
     constexpr bool kTwoPass = CW == 1 && NCH > 32;
     using R = Raw<CW>;
     constexpr int RPW = kWave / LPR;
@@ -393,59 +392,39 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
     // come before the row's loads are issued) and the saved statistics.
     typename R::T rdy[NCH], rx[NCH], gr[NCH];
     float mu = 0.0f, rs = 0.0f;
+    // Every load is unconditional, at an index clamped into its tensor (past
+    // the row's end a lane reads the row's last vector or element, past the
+    // last row a wave reads the last row), and values out of range are zeroed
+    // once they arrive: a load under a per-lane condition made the compiler
+    // wait for it, and registers zeroed ahead of the loads delay every wave
+    // on the SIMD.
     auto fetch = [&](uint32_t row) {
         const bool ok = row < rows;
-        if constexpr (kClamped) {
-            // Element-wise path: unconditional loads at clamped indices, as in
-            // the forward (the vector path below does the same per chunk).
-            const uint32_t rc = ok ? row : rows - 1;
-            const size_t cbase = static_cast<size_t>(rc) * h;
+        const uint32_t rc = ok ? row : rows - 1;
+        const size_t base = static_cast<size_t>(rc) * h;
 #pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const uint32_t c = l + j * LPR;
-                const uint32_t cc = c < h ? c : h - 1;
-                rdy[j] = R::load(dy, cbase + cc);
-                rx[j] = R::load(x, cbase + cc);
-                gr[j] = R::load_cached(gamma, cc);
-            }
-            mu = mean[rc];
-            rs = rstd[rc];
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const bool in = ok && l + j * LPR < h;
-                rdy[j] = in ? rdy[j] : R::zero();
-                rx[j] = in ? rx[j] : R::zero();
-                gr[j] = in ? gr[j] : R::zero();
-            }
-            mu = ok ? mu : 0.0f;
-            rs = ok ? rs : 0.0f;
-        } else {
-            const uint32_t rc = ok ? row : rows - 1;
-            const size_t base = static_cast<size_t>(rc) * h;
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const uint32_t c = (l + j * LPR) * CW;
-                const uint32_t cc = c < h ? c : h - CW;
-                rdy[j] = R::load(dy, base + cc);
-                rx[j] = R::load(x, base + cc);
-            }
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const uint32_t c = (l + j * LPR) * CW;
-                gr[j] = R::load_cached(gamma, c < h ? c : h - CW);
-            }
-            mu = mean[rc];
-            rs = rstd[rc];
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const bool in = ok && (l + j * LPR) * CW < h;
-                rdy[j] = in ? rdy[j] : R::zero();
-                rx[j] = in ? rx[j] : R::zero();
-                gr[j] = in ? gr[j] : R::zero();
-            }
-            mu = ok ? mu : 0.0f;
-            rs = ok ? rs : 0.0f;
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            const uint32_t cc = c < h ? c : h - CW;
+            rdy[j] = R::load(dy, base + cc);
+            rx[j] = R::load(x, base + cc);
         }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const uint32_t c = (l + j * LPR) * CW;
+            gr[j] = R::load_cached(gamma, c < h ? c : h - CW);
+        }
+        mu = mean[rc];
+        rs = rstd[rc];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const bool in = ok && (l + j * LPR) * CW < h;
+            rdy[j] = in ? rdy[j] : R::zero();
+            rx[j] = in ? rx[j] : R::zero();
+            gr[j] = in ? gr[j] : R::zero();
+        }
+        mu = ok ? mu : 0.0f;
+        rs = ok ? rs : 0.0f;
     };
     // Parks this wave's column sums in its LDS slot.  Called right after the
     // last row's accumulation, so the LDS writes overlap that row's dx work
