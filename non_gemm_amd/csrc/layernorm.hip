@@ -70,10 +70,11 @@ struct Chunk<1> {
     }
 };
 
-// Raw 16-byte (or 2-byte) row chunks.  A conditional load goes into a
-// register set that was zeroed beforehand, so no instruction writes those
-// registers after the load and every load of a row stays in flight until the
-// first arithmetic that needs it.
+// Raw 16-byte (or 2-byte) row chunks.  In the forward's vector path a
+// conditional load goes into a register set that was zeroed beforehand, so
+// no instruction writes those registers after the load and every load of a
+// row stays in flight until the first arithmetic that needs it; the backward
+// loads unconditionally at clamped indices instead (its row pass says why).
 template <int CW>
 struct Raw;
 template <>
