@@ -7,6 +7,8 @@ Bars (written here, not in the oracle):
 Shapes cover several tiles, ragged tails, the vector and element-wise paths,
 the empty case and the workloads' full sizes.
 """
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -427,6 +429,11 @@ def test_layernorm_bwd(ls, rows, h):
     assert_fp16(host(dx), rdx, tag + " dx")
     assert_fp16(host(dg), rdg, tag + " dgamma")
     assert_fp16(host(db), rdb, tag + " dbeta")
+    # the row kernel writes one partial row per block, and the finalisation
+    # reads (clamped) up to as many rows as the workspace holds: the grid in
+    # the dispatch name never exceeds that count
+    grid = int(re.search(r"_g(\d+)$", last_dispatch()).group(1))
+    assert 1 <= grid <= (ls.layernorm_bwd_workspace_bytes(rows, h) - 256) // (8 * h), tag
     # the column reduction has a fixed order: a second run is bit-identical
     dx2, dg2, db2 = ls.layernorm_bwd(dev(dy), dev(x), dev(gamma), dev(mean), dev(rstd))
     assert np.array_equal(host(dg2), host(dg)) and np.array_equal(host(db2), host(db))
