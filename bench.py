@@ -42,9 +42,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 # The dominant kernel: the one with the largest share of the chain's time --
-# the LayerNorm backward's row kernel, launched twice per step; the fused
-# block's kernel (also twice per step) takes as much time within a few
-# percent, at a higher fraction of its roofline, so the lower one is reported.
+# the LayerNorm backward's row kernel, launched twice per step.  The fused
+# block's kernel (also twice per step) takes about as much time, a few percent
+# more in the kernel trace, at a higher fraction of its roofline; the lower
+# one is reported.
 # (The largest single launch, bias+ReLU+dropout, is reported beside it.)
 DOMINANT = "layernorm_bwd"
 DOMINANT_SHAPE = "[4096,768]"
