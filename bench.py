@@ -4,19 +4,23 @@ One step is one pass of the layer's non-GEMM hot path over a 4096-token batch
 (32 sequences x 128, hidden 768, 12 heads, FFN 3072, fp16 storage, fp32
 arithmetic, dropout 0.1):
 
-  softmax fwd [32,12,128,128] -> bias+dropout+residual [4096,768] -> LayerNorm fwd
-  -> bias+ReLU+dropout [4096,3072] -> bias+dropout+residual [4096,768] -> LayerNorm fwd
-  -> LayerNorm bwd x2 -> softmax bwd
+  softmax fwd [32,12,128,128] -> bias+dropout+residual -> LayerNorm [4096,768]
+  (one fused call) -> bias+ReLU+dropout [4096,3072] -> the fused block again
+  -> LayerNorm bwd input gradients x2 -> both LayerNorms' parameter gradients
+  (one call) -> softmax bwd
 
 Inputs are synthetic (seeded, shaped like the layer) and resident in HBM before
-the timed region.  R independent buffer sets (> 2 GB in total) are rotated so
-that no step finds its tensors in the 256 MB Infinity Cache.  Each set's step is
-captured as one HIP graph.  Every 8th timed step is replayed split around the
-first LayerNorm backward, the operator whose row kernel takes the largest share
-of the step (two launches of it per step), which is then called directly on the
-same stream with a pair of HIP events attached to its row kernel's launch
-(hipExtLaunchKernel records them when the kernel starts and ends): the events
-sample that kernel's duration live inside the timed region (the roofline line).
+the timed region.  R independent buffer sets (> 2 GB in total; 12 by default,
+one per layer of BERT-base) are rotated so that no step finds its tensors in
+the 256 MB Infinity Cache.  The timed steps are replayed as HIP graphs of G
+consecutive steps (one step per set in turn; G = R by default, a training
+iteration's layers in one graph).  Every few timed graphs one is replayed
+split around its first LayerNorm backward, the operator whose row kernel
+takes the largest share of the step (two launches of it per step), which is
+then called directly on the same stream with a pair of HIP events attached
+to its row kernel's launch (hipExtLaunchKernel records them when the kernel
+starts and ends): the events sample that kernel's duration live inside the
+timed region (the roofline line).
 The largest single launch, bias+ReLU+dropout, is reported beside it from the
 cold per-kernel timing.
 
@@ -24,7 +28,7 @@ Output: one JSON line.  `value` is algorithmic chain bytes per second (the
 fused-minimum bytes: every input read once, every output written once, the
 dropout mask regenerated, not stored) and `tokens_per_s` the chain rate.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph-steps G] [--no-cpu] [--no-extra]
        python bench.py --summarize-counters FETCH.csv WRITE.csv   (writes profiles/)
 """
 
@@ -285,6 +289,16 @@ def capture_items(torch, items, cap_stream, check, side):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap_stream):
         issue(torch, items, check, side)
+    return g
+
+
+def capture_steps(torch, runs, cap_stream, check, side):
+    """One HIP graph of several steps (ChainSets) in turn, each step's
+    side-stream items joined before the next step."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap_stream):
+        for s in runs:
+            issue(torch, s.launches, check, side)
     return g
 
 
@@ -1125,8 +1139,9 @@ def stored_traffic():
 def transformer_big_chain(torch, lib, check, cap_stream, side, p, seed, eps, nsets=3, reps=20):
     """The Transformer-big layer (8192 tokens, hidden 1024, 16 heads, FFN 4096)
     through the same calls as the BERT-base step plus the embedding forward and backward
-    (vocabulary 32768, Zipf ids, fp32 gradient accumulated), one HIP graph per
-    rotated buffer set (about 0.9 GB each)."""
+    (vocabulary 32768, Zipf ids, fp32 gradient accumulated) on 3 rotated
+    buffer sets (about 0.9 GB each), all three steps in one HIP graph (and,
+    for comparison, one graph per step)."""
     import numpy as np
 
     import synth
@@ -1154,16 +1169,20 @@ def transformer_big_chain(torch, lib, check, cap_stream, side, p, seed, eps, nse
                             synth.SITE_EMBEDDING, 0, S)))
         s.run(check, side)
     torch.cuda.synchronize()
-    graphs = [capture_items(torch, s.launches, cap_stream, check, side) for s in sets]
-    us = replay_us(torch, graphs, reps)
+    whole = [capture_steps(torch, sets, cap_stream, check, side)]
+    us = replay_us(torch, whole, reps) / nsets
+    per_step = [capture_steps(torch, [s], cap_stream, check, side) for s in sets]
+    us1 = replay_us(torch, per_step, reps)
     nbytes = total + emb_f + emb_b
     out = {"shape": "8192 tokens (32 x 256), hidden 1024, 16 heads, FFN 4096, vocab 32768",
            "calls_per_step": len(sets[0].launches),
            "kernels_per_step": len(sets[0].launches),
            "us_per_step": round(us, 2), "bytes_per_step": nbytes,
            "GB/s": round(nbytes / us / 1e3, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
-           "rotated_sets": nsets}
-    del graphs, sets, keep
+           "rotated_sets": nsets, "steps_per_graph": nsets,
+           "one_graph_per_step": {"us_per_step": round(us1, 2), "GB/s": round(nbytes / us1 / 1e3, 1),
+                                  "tokens_per_s": round(T / (us1 * 1e-6), 1)}}
+    del whole, per_step, sets, keep
     torch.cuda.empty_cache()
     return out
 
@@ -1223,45 +1242,44 @@ def attainable(torch, lib, check, cap_stream, dom_bytes, sizes=None):
     return out
 
 
-def step_variants(torch, lib, check, cap_stream, p, seed, eps, nsets=12, reps=20):
-    """The same BERT-base step in other forms, each on its own rotated sets:
-    bias+dropout+residual and LayerNorm as two operators each and each
-    LayerNorm's parameter gradients in a call of their own (unfused); the
-    fused step with each LayerNorm's parameter gradients in a call of their
-    own; and the fused step with the batched parameter gradients on a side
-    stream (a branch of the graph, joined at the end of the step)."""
+def step_variants(torch, lib, check, cap_stream, p, seed, eps, nsets=12, graph_steps=12, reps=20):
+    """The same BERT-base step in other forms, each on its own rotated sets
+    and, like the timed steps, in HIP graphs of graph_steps steps: the
+    measured step in one graph per step; bias+dropout+residual and LayerNorm
+    as two operators each and each LayerNorm's parameter gradients in a call
+    of their own (unfused); the fused step with each LayerNorm's parameter
+    gradients in a call of their own; and the fused step with the batched
+    parameter gradients on a side stream (a branch of the graph, joined at
+    the end of each step)."""
     import synth
     shape = synth.C3
     out = {}
     side = torch.cuda.Stream()         # default priority, like every stream here
-    for key, fused, batched, side_ in (("unfused", False, False, None),
-                                       ("fused_parameter_gradients_per_layernorm", True, False, None),
-                                       ("fused_parameter_gradients_on_side_stream", True, True, side)):
+    for key, fused, batched, side_, g_steps in (
+            ("one_graph_per_step", True, True, None, 1),
+            ("unfused", False, False, None, graph_steps),
+            ("fused_parameter_gradients_per_layernorm", True, False, None, graph_steps),
+            ("fused_parameter_gradients_on_side_stream", True, True, side, graph_steps)):
         sets, per, counts, total = build_sets(torch, lib, shape, nsets, p, seed, eps, fused=fused,
                                               batched_params=batched)
         for s in sets:
             s.run(check, side_)
-        graphs = [capture_items(torch, s.launches, cap_stream, check, side_) for s in sets]
-        us = replay_us(torch, graphs, reps)
-        out[key] = {"calls_per_step": len(sets[0].launches), "us_per_step": round(us, 2), "bytes_per_step": total,
-                    "GB/s": round(total / us / 1e3, 1), "tokens_per_s": round(shape.tokens / (us * 1e-6), 1)}
+        graphs = [capture_steps(torch, sets[i:i + g_steps], cap_stream, check, side_)
+                  for i in range(0, nsets, g_steps)]
+        us = replay_us(torch, graphs, reps) / g_steps
+        out[key] = {"calls_per_step": len(sets[0].launches), "steps_per_graph": g_steps, "us_per_step": round(us, 2),
+                    "bytes_per_step": total, "GB/s": round(total / us / 1e3, 1),
+                    "tokens_per_s": round(shape.tokens / (us * 1e-6), 1)}
         del graphs, sets
         torch.cuda.empty_cache()
     return out
 
 
-def warm_chain_us(torch, s, cap_stream, check, side, reps=100):
-    """One buffer set replayed back to back: the chain with its tensors cache-resident."""
-    g = capture_items(torch, s.launches, cap_stream, check, side)
-    g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / reps
+def warm_chain_us(torch, s, cap_stream, check, side, graph_steps=1, reps=100):
+    """One buffer set stepped again and again (graph_steps steps per graph):
+    the chain with its tensors cache-resident."""
+    g = capture_steps(torch, [s] * graph_steps, cap_stream, check, side)
+    return replay_us(torch, [g], reps) / graph_steps
 
 
 def main():
@@ -1270,9 +1288,11 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sets", type=int, default=12, help="rotated buffer sets (cold-cache measurement)")
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="steps per HIP graph in the timed region (a divisor of --sets; default: --sets)")
     ap.add_argument("--sample-every", type=int, default=0,
-                    help="every Nth timed step runs the dominant kernel between its own events "
-                         "(default: about 25-32 samples over the timed steps)")
+                    help="every Nth timed graph runs the dominant kernel between its own events "
+                         "(default: about 20-30 samples over the timed region)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the embedding / Adam rows")
     ap.add_argument("--eager", action="store_true",
@@ -1356,59 +1376,87 @@ def main():
         s.run(check, side)
     torch.cuda.synchronize()
 
-    # Per set: one graph of the whole step, and the same step split around the
-    # dominant kernel (graph A, the kernel launched directly between two
-    # fence-free events, graph B).  Every SAMPLE-th step of the timed region
-    # is a split one, so the events sample the kernel live while the other
-    # steps run as single graphs.
+    # The timed steps run as HIP graphs of G consecutive steps each (G =
+    # --graph-steps, by default every rotated set in turn: the 12 layers of
+    # BERT-base, each on its own buffers, as a whole training iteration would
+    # be captured).  A graph's launch costs about 5 us of its own, so one
+    # graph per step carries that cost in every step (step_variants reports
+    # that form too).  Every SAMPLE-th graph of the timed region runs split
+    # around its first step's dominant kernel (graph A, the kernel launched
+    # directly between two fence-free events, graph B), so the events sample
+    # the kernel live while the other graphs run whole.
     dom_idx = [i for i, l in enumerate(sets[0].launches) if l[0] == DOMINANT][0]
     cap_stream = torch.cuda.Stream()
-
-    def capture(s, lo, hi):
-        return capture_items(torch, s.launches[lo:hi], cap_stream, check, side)
     n_launch = len(sets[0].launches)
-    graphs = [(capture(s, 0, n_launch), capture(s, 0, dom_idx), capture(s, dom_idx + 1, n_launch)) for s in sets]
-    torch.cuda.synchronize()
+    G = args.graph_steps or len(sets)
+    if not 1 <= G <= len(sets) or len(sets) % G:
+        print(f"--graph-steps {G} must divide --sets {len(sets)}", file=sys.stderr)
+        return 2
     stream = torch.cuda.current_stream()
     S = stream.cuda_stream
-    dom = [(s.launches[dom_idx][2], s.launches[dom_idx][3][:-1] + (S,)) for s in sets]
-    # A sampled step (two graphs around a direct launch) costs about 1 us more
-    # than a whole-step graph, so only every SAMPLE-th step is one: enough
-    # samples for the kernel's mean, little of that cost in the step time.
-    SAMPLE = args.sample_every if args.sample_every > 0 else max(1, min(32, args.steps // 24))
 
-    def step(i, ev=None):
-        s = sets[i % len(sets)]
-        g_full, g_a, g_b = graphs[i % len(graphs)]
-        sampled = ev is not None and i % SAMPLE == 0
-        if not args.eager and not sampled:
+    def chunks(n_steps):
+        """(first step, steps) of each graph over n_steps steps."""
+        return [(i, min(G, n_steps - i)) for i in range(0, n_steps, G)]
+
+    graphs = {}                        # (first set, steps) -> (whole, A, B, dominant call)
+
+    def graph_of(i, n):
+        key = (i % len(sets), n)
+        if key not in graphs:
+            run = [sets[(key[0] + k) % len(sets)] for k in range(n)]
+            items = [it for s in run for it in s.launches]
+            d = run[0].launches[dom_idx]
+            graphs[key] = (capture_items(torch, items, cap_stream, check, side),
+                           capture_items(torch, items[:dom_idx], cap_stream, check, side),
+                           capture_items(torch, items[dom_idx + 1:], cap_stream, check, side),
+                           (d[2], d[3][:-1] + (S,)))
+        return graphs[key]
+    K = args.steps
+    for i, n in chunks(args.warmup) + chunks(K):     # every graph captured before the timed region
+        graph_of(i, n)
+    torch.cuda.synchronize()
+    # A sampled graph (two graphs around a direct launch) costs several us
+    # more than a whole one, so only every SAMPLE-th graph is split: about
+    # 20-30 samples for the kernel's mean, little of that cost in the step.
+    n_graphs = len(chunks(K))
+    SAMPLE = args.sample_every if args.sample_every > 0 else max(1, min(-(-32 // G), n_graphs // 24))
+
+    def run_graph(c, i, n, ev=None):
+        """Steps i .. i+n-1 (graph c of the region); with ev, a sampled one if c % SAMPLE == 0."""
+        sampled = ev is not None and c % SAMPLE == 0
+        if args.eager:
+            for k in range(n):
+                s = sets[(i + k) % len(sets)]
+                if sampled and k == 0:
+                    issue(torch, s.launches[:dom_idx], check, side)
+                    ev.arm(c // SAMPLE, lib)
+                    fn, a = s.launches[dom_idx][2], s.launches[dom_idx][3][:-1] + (S,)
+                    check(DOMINANT, fn(*a))
+                    issue(torch, s.launches[dom_idx + 1:], check, side)
+                else:
+                    issue(torch, s.launches, check, side)
+            return
+        g_full, g_a, g_b, (fn, a) = graph_of(i, n)
+        if not sampled:
             g_full.replay()
             return
-        fn, a = dom[i % len(dom)]
-        if args.eager:
-            issue(torch, s.launches[:dom_idx], check, side)
-        else:
-            g_a.replay()
-        if sampled:
-            ev.arm(i // SAMPLE, lib)
-        fn(*a)
-        if args.eager:
-            issue(torch, s.launches[dom_idx + 1:], check, side)
-        else:
-            g_b.replay()
+        g_a.replay()
+        ev.arm(c // SAMPLE, lib)
+        check(DOMINANT, fn(*a))
+        g_b.replay()
 
-    for i in range(args.warmup):
-        step(i)
+    for c, (i, n) in enumerate(chunks(args.warmup)):
+        run_graph(c, i, n)
     torch.cuda.synchronize()
 
-    K = args.steps
-    kev = KernelEvents((K + SAMPLE - 1) // SAMPLE)
+    kev = KernelEvents((n_graphs + SAMPLE - 1) // SAMPLE)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record()
-    for i in range(K):
-        step(i, kev)
+    for c, (i, n) in enumerate(chunks(K)):
+        run_graph(c, i, n, kev)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -1470,7 +1518,7 @@ def main():
                    "timing": "cold: a graph of back-to-back launches over the rotated sets, events around it"}
     warm_us = None
     if not args.no_info:
-        warm_us = warm_chain_us(torch, sets[0], cap_stream, check, side)
+        warm_us = warm_chain_us(torch, sets[0], cap_stream, check, side, G)
     dispatch = {}
     for it in sets[0].launches:
         name, _, fn, args_ = it[:4]
@@ -1480,7 +1528,7 @@ def main():
     del graphs, sets
     torch.cuda.empty_cache()
     variants = None if args.no_info else step_variants(torch, lib, check, cap_stream, p, seed, eps,
-                                                       nsets=args.sets)
+                                                       nsets=args.sets, graph_steps=G)
     copy_sizes = {**{f"{k} C3": per[k] for k in kernels}, **other_rows_bytes()}
     reach = None if args.no_info else attainable(torch, lib, check, cap_stream, dom_bytes, copy_sizes)
     if reach is not None:
@@ -1512,6 +1560,7 @@ def main():
         "config": {"workload": "bert-base-layer-non-gemm-chain", "tokens": shape.tokens, "batch": shape.batch,
                    "seq_len": shape.seq, "hidden": shape.hidden, "heads": shape.heads, "ffn": shape.ffn,
                    "dropout_p": p, "chain_bytes_per_step": total, "rotated_sets": args.sets,
+                   "steps_per_graph": G,
                    "footprint_bytes": footprint, "launches_per_step": n_launch,
                    "kernels_per_step": n_launch,
                    "fused_bias_dropout_residual_layernorm": True},
@@ -1520,7 +1569,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": stored_traffic(), "algorithmic_bytes": dom_bytes,
                      "avg_duration_us": round(dom_us, 3),
-                     "samples": len(range(0, K, SAMPLE)), "sample_every": SAMPLE,
+                     "samples": (n_graphs + SAMPLE - 1) // SAMPLE, "sample_every_graphs": SAMPLE,
                      # the whole operator (row kernel, then its parameter finalisation on the same stream),
                      # from the cold per-operator timing
                      "op_level": None if DOMINANT not in kernels else {
