@@ -389,13 +389,16 @@ struct BwdBounds {
     static constexpr int kMaxThreads = bwd_max_threads(NCH, CW);
 };
 constexpr size_t kBwdLdsBudget = 128 * 1024;
+// Columns per tile of the partial rows (one 128-byte line of floats).
+constexpr uint32_t kPartTile = 32;
 
 template <int LPR, int NCH, int CW>
 __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kernel(half_t* dx, float* partial,
                                                                 uint32_t* header, const half_t* dy,
                                                                 const half_t* x, const half_t* gamma,
                                                                 const float* mean, const float* rstd,
-                                                                uint32_t rows, uint32_t h, float inv_h) {
+                                                                uint32_t rows, uint32_t h, uint32_t slots,
+                                                                float inv_h) {
     // The partial-row count, for the finalisation (which may run as a
     // separate call).
     if (blockIdx.x == 0 && threadIdx.x == 0) header[0] = gridDim.x;
@@ -638,22 +641,30 @@ __global__ __launch_bounds__((BwdBounds<NCH, CW>::kMaxThreads)) void ln_bwd_kern
     for (r0 += stride; r0 < rows; r0 += stride) row_pass(r0, std::integral_constant<bool, false>{});
     }
     __syncthreads();
-    float* out = partial + static_cast<size_t>(blockIdx.x) * 2 * h;
+    // The block's partial row, in tiles of kPartTile columns: column col of block b
+    // at t0 * slots + b * wt + (col - t0), where t0 is the tile's first
+    // column and wt its width (kPartTile, less for a ragged last tile), so tile t
+    // holds the slots rows of its columns contiguously; slots = the partial
+    // rows the workspace holds (>= gridDim.x), and the last tile ends at
+    // slots * 2h.
     for (uint32_t col = threadIdx.x; col < 2 * h; col += blockDim.x) {
         float t = 0.0f;
         for (int w = 0; w < nwaves; ++w) t += lds[static_cast<size_t>(w) * 2 * h + col];
-        out[col] = t;
+        const uint32_t t0 = col / kPartTile * kPartTile, wt = min(kPartTile, 2 * h - t0);
+        partial[static_cast<size_t>(t0) * slots + static_cast<size_t>(blockIdx.x) * wt + (col - t0)] = t;
     }
 }
 
-// Column finalisation over the [nblocks][2h] partials: column c of the 2h
-// (dgamma then dbeta) is summed by 32 thread slices (slice s takes blocks
+// Column finalisation over the nblocks partial rows of 2h columns (dgamma
+// then dbeta): column c is summed by 32 thread slices (slice s takes blocks
 // s, s+32, ...), then the 32 slice sums in order.  nblocks <= 256, so every
 // thread issues at most 8 independent loads (1024-thread blocks: measured
-// 0.3-0.4 us per BERT-base step faster than 16 slices of 16 loads).  A
-// block takes 32 columns, so each partial row is read in whole 128-byte
-// lines.
-constexpr int kFinCols = 32;
+// 0.3-0.4 us per BERT-base step faster than 16 slices of 16 loads).  The
+// partials are stored in tiles of kPartTile columns (see the row kernel's store),
+// and a block takes one tile, a single contiguous run of memory (measured
+// 9.43-9.44 against 9.54-9.55 us per [4096, 768] operator call with the
+// partial rows stored whole, 2h floats apart).
+constexpr int kFinCols = kPartTile;
 constexpr int kFinSlices = 32;
 constexpr unsigned kMaxBwdBlocks = 256;
 constexpr int kFinLoads = kMaxBwdBlocks / kFinSlices;
@@ -685,7 +696,7 @@ __global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
     const uint32_t h = jobs.h[j], max_blocks = jobs.max_blocks[j];
     const float* partial = jobs.partial[j];
     const int cl = threadIdx.x % kFinCols, sl = threadIdx.x / kFinCols;
-    const uint32_t c = (blockIdx.x - jobs.first_block[j]) * kFinCols + cl;
+    const uint32_t t0 = (blockIdx.x - jobs.first_block[j]) * kFinCols, c = t0 + cl;
     const uint32_t w = 2 * h;
     float v[kFinLoads];
     uint32_t nblocks = 0;
@@ -694,7 +705,8 @@ __global__ __launch_bounds__(kFinCols * kFinSlices) void ln_bwd_finalize_kernel(
 #pragma unroll
         for (int i = 0; i < kFinLoads; ++i) {
             const uint32_t b = sl + i * kFinSlices;
-            v[i] = partial[static_cast<size_t>(b < max_blocks ? b : max_blocks - 1) * w + cc];
+            v[i] = partial[static_cast<size_t>(t0) * max_blocks +
+                           static_cast<size_t>(b < max_blocks ? b : max_blocks - 1) * min(kPartTile, w - t0) + (cc - t0)];
         }
         nblocks = min(jobs.header[j][0], max_blocks);
     } else {
@@ -827,7 +839,7 @@ BwdLaunch bwd_launch(int64_t rows, int64_t h, const LnShape& s) {
             return fail(LS_ERR_HIP, "%s: cannot reserve %zu bytes of LDS", name, bl.lds_bytes); \
         launch_kernel(ln_bwd_kernel<LPR, NCH, CW>, dim3(bl.grid), dim3(bl.waves * kWave),         \
                       bl.lds_bytes, st, dx16, part, hdr, dy16, x16, g16, mean, rstd, r32, h32, \
-                      1.0f / static_cast<float>(h32));    \
+                      bwd_max_blocks(r32), 1.0f / static_cast<float>(h32));    \
     } while (0)
 
 #define LS_LN_TABLE(M)                                                                          \
