@@ -292,6 +292,19 @@ def capture_items(torch, items, cap_stream, check, side):
     return g
 
 
+def graph_chunks(n_steps, steps_per_graph):
+    """(first step, steps) of each graph when n_steps steps run as graphs of
+    steps_per_graph consecutive steps; the last graph holds the steps left
+    over, so the graphs cover exactly n_steps steps."""
+    return [(i, min(steps_per_graph, n_steps - i)) for i in range(0, n_steps, steps_per_graph)]
+
+
+def sample_every_graphs(n_graphs, steps_per_graph):
+    """Every how many timed graphs one is split to time the dominant kernel
+    live: about 24 samples or more, and at least one every ~32 steps' worth."""
+    return max(1, min(-(-32 // steps_per_graph), n_graphs // 24))
+
+
 def capture_steps(torch, runs, cap_stream, check, side):
     """One HIP graph of several steps (ChainSets) in turn, each step's
     side-stream items joined before the next step."""
@@ -1396,8 +1409,7 @@ def main():
     S = stream.cuda_stream
 
     def chunks(n_steps):
-        """(first step, steps) of each graph over n_steps steps."""
-        return [(i, min(G, n_steps - i)) for i in range(0, n_steps, G)]
+        return graph_chunks(n_steps, G)
 
     graphs = {}                        # (first set, steps) -> (whole, A, B, dominant call)
 
@@ -1420,7 +1432,7 @@ def main():
     # more than a whole one, so only every SAMPLE-th graph is split: about
     # 20-30 samples for the kernel's mean, little of that cost in the step.
     n_graphs = len(chunks(K))
-    SAMPLE = args.sample_every if args.sample_every > 0 else max(1, min(-(-32 // G), n_graphs // 24))
+    SAMPLE = args.sample_every if args.sample_every > 0 else sample_every_graphs(n_graphs, G)
 
     def run_graph(c, i, n, ev=None):
         """Steps i .. i+n-1 (graph c of the region); with ev, a sampled one if c % SAMPLE == 0."""

@@ -5,6 +5,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 import bench
 import synth
@@ -66,3 +67,24 @@ def test_same_size_copy_covers_every_row():
         assert row in rows and rows[row] > 0
     for key in ("tiny_chain C1 (3 calls)", "attention_softmax_fwd C2", "attention_softmax_bwd C2"):
         assert rows[key] > 0
+
+
+@pytest.mark.parametrize("steps,g", [(1000, 12), (200, 12), (12, 12), (5, 12), (1, 12), (0, 12), (1000, 1),
+                                     (50, 4), (13, 6)])
+def test_graph_chunks_cover_every_step_once(steps, g):
+    chunks = bench.graph_chunks(steps, g)
+    covered = [i + k for i, n in chunks for k in range(n)]
+    assert covered == list(range(steps))
+    assert all(1 <= n <= g for _, n in chunks)
+    assert all(n == g for _, n in chunks[:-1])
+    assert all(i % g == 0 for i, _ in chunks)
+
+
+@pytest.mark.parametrize("steps,g", [(1000, 12), (200, 12), (1000, 1), (24, 1), (5, 12), (100000, 12)])
+def test_live_samples_stay_bounded(steps, g):
+    n_graphs = len(bench.graph_chunks(steps, g))
+    every = bench.sample_every_graphs(n_graphs, g)
+    samples = -(-n_graphs // every)
+    assert every >= 1
+    assert every * g < 32 + g                 # a sample at least every ~32 steps
+    assert samples >= min(n_graphs, 24)       # enough samples for the mean
