@@ -710,6 +710,26 @@ def test_softmax_fwd_dense(ls, shape):
         assert np.array_equal(np.argmax(yy[unique], 1), np.argmax(r[unique], 1)), tag
 
 
+@pytest.mark.parametrize("shape,name", [((8, 12, 128, 128), "lpr16_nch1_v8"), ((32, 12, 128, 128), "lpr8_nch2_v8"),
+                                        ((2, 2, 33, 120), "lpr16_nch1_v8"), ((64, 8, 64, 72), "lpr8_nch2_v8")])
+def test_softmax_row_mapping_follows_row_count(ls, shape, name):
+    """Rows of 72-128 keys: 16 lanes x 1 vector while 8 x 2 would give fewer
+    than 4096 waves (under 32768 rows), 8 x 2 from there on; same results
+    either way, forward and backward."""
+    g = np.random.default_rng(sum(shape) + 5)
+    x = synth.normal16(g, shape, 3.0)
+    y = host(ls.softmax_fwd(dev(x)))
+    assert last_dispatch() == "softmax_fwd/" + name
+    assert_fp16(y, oracle.softmax_fwd(x), f"softmax_fwd {shape} [{name}]")
+    dy = synth.normal16(g, shape, 1.0)
+    yv = oracle.softmax_fwd(x)
+    k = shape[-1]
+    dx = host(ls.softmax_bwd(dev(yv), dev(dy)))
+    assert last_dispatch() == "softmax_bwd/" + name
+    ref = oracle.softmax_bwd(yv.reshape(-1, k), dy.reshape(-1, k)).reshape(shape)
+    assert_fp16(dx, ref, f"softmax_bwd {shape} [{name}]")
+
+
 # the dense C2 case (no lengths, not causal) is the first of SM_SHAPES
 @pytest.mark.parametrize("causal,with_lengths", [(False, True), (True, True), (True, False)])
 def test_softmax_fwd_c2_masked(ls, causal, with_lengths):
